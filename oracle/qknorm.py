@@ -1,0 +1,172 @@
+"""Layerwise QK-Norm, written out in float64 (test infrastructure only).
+
+Source: "SwiftQK: Fast and Communication-Efficient Tensor Parallelism for
+Query-Key Normalization" (arXiv 2608.09160v1), arXiv HTML page.
+
+Layerwise QK-Norm normalizes each token's whole projected Q vector with one
+RMS factor, and separately its whole projected K vector with another (the
+paper's introduction contrasts this with headwise QK-Norm, one factor per
+head). For one vector x of full width H (RMS-Norm, Eq. 1, read as stated in
+the package docstring):
+
+    y_j = x_j * gamma_j / sqrt( (sum_i x_i**2) / H + eps )
+
+Phase A of the paper observes that the denominator needs only the sum of
+squares, which splits over contiguous column shards: each shard contributes
+its own sum, and the global sum is the sum of the shard sums. Phase B and the
+final scaling multiply the shard by gamma and then by the global factor.
+
+Each step below is one function so that a reader can check it against those
+passages by eye. There is no blocking, fusion or reordering: every reduction
+is a plain ``numpy.sum`` over float64 values.
+"""
+
+import numpy as np
+
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+
+
+# --------------------------------------------------------------------------
+# input decoding
+# --------------------------------------------------------------------------
+def decode_input(a, dtype):
+    """Exact float64 value of an input array.
+
+    ``dtype == "bf16"``: ``a`` holds bf16 bit patterns (uint16).
+    ``dtype == "f32"``:  ``a`` holds float32 values.
+    """
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def eps_as_passed(eps):
+    """The kernel receives eps as float32; the oracle uses that exact value."""
+    return float(np.float32(eps))
+
+
+# --------------------------------------------------------------------------
+# Phase A: per-shard partial sums of squares, then their combination
+# --------------------------------------------------------------------------
+def shard_sum_of_squares(x, shards):
+    """partial[s, t] = sum over the columns j of shard s of x[t, j]**2.
+
+    ``x`` is float64 [T, h]; shard s covers the contiguous columns
+    [s*h/S, (s+1)*h/S). Returns float64 [S, T]. (Phase A: the local squared
+    sum of a hidden-dimension shard.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, h = x.shape
+    if shards < 1 or h % shards:
+        raise ValueError(f"width {h} is not divisible into {shards} shards")
+    w = h // shards
+    out = np.empty((shards, T), dtype=np.float64)
+    for s in range(shards):
+        out[s] = np.sum(x[:, s * w:(s + 1) * w] ** 2, axis=1)
+    return out
+
+
+def combine_partials(partials):
+    """Global sum of squares per token: the sum of the partials over axis 0.
+
+    (Phase A: aggregating the shard sums recovers the global squared sum.)
+    """
+    return np.sum(np.asarray(partials, dtype=np.float64), axis=0)
+
+
+# --------------------------------------------------------------------------
+# the RMS factor and the scaling (Eq. 1; Phase B and the final scaling)
+# --------------------------------------------------------------------------
+def rms_denominator(ss, h_full, eps):
+    """sqrt(ss / H + eps): the denominator of Eq. 1 for each token."""
+    return np.sqrt(np.asarray(ss, dtype=np.float64) / float(h_full) + eps)
+
+
+def scale_rows(x, gamma, denom):
+    """y[t, j] = x[t, j] * gamma[j] / denom[t]."""
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    return x * gamma[None, :] / np.asarray(denom, dtype=np.float64)[:, None]
+
+
+def layerwise_rmsnorm(x, gamma, eps, shards=1):
+    """RMS-Norm of every row of x over its full width, via S shard partials.
+
+    Returns (y [T, h], partials [S, T]), both float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    partials = shard_sum_of_squares(x, shards)
+    ss = combine_partials(partials)
+    denom = rms_denominator(ss, x.shape[1], eps)
+    return scale_rows(x, gamma, denom), partials
+
+
+def apply_with_stats(x, gamma, planes, h_full, eps):
+    """Normalize a local slice x with sums of squares supplied from outside.
+
+    ``planes`` is [P, T]: P partial (or already combined, P = 1) sums of
+    squares per token, which are added to form the global sum; ``h_full`` is
+    the full vector width H that Eq. 1 divides by (not the local width).
+    """
+    ss = combine_partials(planes)
+    denom = rms_denominator(ss, h_full, eps)
+    return scale_rows(x, gamma, denom)
+
+
+# --------------------------------------------------------------------------
+# the three calls of the library, on the same inputs the library receives
+# --------------------------------------------------------------------------
+class QKResult:
+    """Oracle outputs for one call.
+
+    ``yq``/``yk``: float64 results. ``yq_bits``/``yk_bits``: the bf16 result
+    rounded once from float64 (bf16 I/O only, else None). ``pq``/``pk``:
+    float64 shard partials [S, T] (fused only, else None).
+    """
+
+    def __init__(self, yq, yk, dtype, pq=None, pk=None):
+        self.yq = yq
+        self.yk = yk
+        self.pq = pq
+        self.pk = pk
+        if dtype == "bf16":
+            self.yq_bits = f64_to_bf16_bits(yq)
+            self.yk_bits = f64_to_bf16_bits(yk)
+        else:
+            self.yq_bits = None
+            self.yk_bits = None
+
+
+def qknorm_fused(xq, xk, gamma_q, gamma_k, dtype, eps, shards):
+    """Layerwise QK-Norm of Q rows and, separately, K rows.
+
+    Each of Q [T, hq] and K [T, hk] is split into ``shards`` equal column
+    shards; H is the whole local width (hq for Q, hk for K).
+    """
+    e = eps_as_passed(eps)
+    yq, pq = layerwise_rmsnorm(decode_input(xq, dtype), decode_input(gamma_q, dtype), e, shards)
+    yk, pk = layerwise_rmsnorm(decode_input(xk, dtype), decode_input(gamma_k, dtype), e, shards)
+    return QKResult(yq, yk, dtype, pq, pk)
+
+
+def qknorm_partial_stats(xq, xk, dtype, shards):
+    """Shard partial sums of squares, float64 [S, 2, T] (index 0 = Q, 1 = K)."""
+    pq = shard_sum_of_squares(decode_input(xq, dtype), shards)
+    pk = shard_sum_of_squares(decode_input(xk, dtype), shards)
+    return np.stack([pq, pk], axis=1)
+
+
+def qknorm_apply_with_stats(xq, xk, gamma_q, gamma_k, dtype, eps, stats, hq_full, hk_full):
+    """Normalize local Q/K slices with given statistics.
+
+    ``stats`` is float32 [P, 2, T]: P planes of sums of squares (index 0 = Q,
+    1 = K) that are added to form each token's global sum; they are read as
+    the exact float64 values of those float32 numbers.
+    """
+    e = eps_as_passed(eps)
+    st = np.asarray(stats, dtype=np.float32).astype(np.float64)
+    yq = apply_with_stats(decode_input(xq, dtype), decode_input(gamma_q, dtype), st[:, 0, :], hq_full, e)
+    yk = apply_with_stats(decode_input(xk, dtype), decode_input(gamma_k, dtype), st[:, 1, :], hk_full, e)
+    return QKResult(yq, yk, dtype)
