@@ -1,0 +1,344 @@
+"""Benchmark of the layerwise QK-Norm hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c4|c5|c2|c3_t1|...]
+
+A step is one pass of the whole path over one batch: for the default
+workload (GQA prefill: T = 8192 tokens, Q 5120 + K 1024 columns normalized,
+V 1024 passed through, bf16 packed [8192, 7168], S = 1) that is one
+qknorm_fused call, out of place into a separate packed buffer. Inputs are
+resident in HBM before timing starts, and the buffer sets rotate over more
+than 1 GiB so that each step streams from HBM rather than from the 256 MB
+Infinity Cache.
+
+Prints one JSON line: tokens/s for the whole job, the roofline of the kernel
+(algorithmic bytes per launch / mean launch time measured with HIP events on
+the launch stream, against the 8 TB/s HBM peak) and the CPU oracle timed on
+the host as a baseline.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+ROTATE_MIN_BYTES = 1 << 30      # > 256 MB Infinity Cache + 8 x 4 MB L2
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["layerwise_qk_norm_qknorm_amd/csrc/qknorm_kernels.hip",
+                  "layerwise_qk_norm_qknorm_amd/csrc/qknorm_internal.hpp",
+                  "layerwise_qk_norm_qknorm_amd/csrc/qknorm_api.cpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def to_device(a, dev):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a.copy()).to(dev)
+
+
+# ----------------------------------------------------------------------------- steps
+class FusedStep:
+    """One qknorm_fused call over a packed QKV buffer set."""
+
+    def __init__(self, w, inp, dev, shards):
+        import torch
+        import layerwise_qk_norm_qknorm_amd as qk
+        self.qk, self.w, self.shards = qk, w, shards
+        x0 = to_device(inp.qkv, dev)
+        per_set = 2 * x0.numel() * x0.element_size()
+        self.n_sets = max(1, -(-ROTATE_MIN_BYTES // per_set))
+        self.sets = []
+        for i in range(self.n_sets):
+            x = x0 if i == 0 else x0.clone()
+            y = torch.zeros_like(x0)
+            self.sets.append((x, y))
+        self.gq = to_device(inp.gamma_q, dev)
+        self.gk = to_device(inp.gamma_k, dev)
+        esz = x0.element_size()
+        self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+        self.footprint = self.n_sets * per_set
+        self.launches = 1
+        self.name = "qknorm_fused"
+
+    def __call__(self, i):
+        x, y = self.sets[i % self.n_sets]
+        hq, hk = self.w.hq, self.w.hk
+        self.qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.shards,
+                             y[:, :hq], y[:, hq:hq + hk])
+
+
+class SplitStep:
+    """One rank's share of the split path: qknorm_partial_stats on the local
+    slice, then qknorm_apply_with_stats with the local plane and the peer
+    planes (computed once before timing, as if received)."""
+
+    def __init__(self, w, inp, dev):
+        import torch
+        import layerwise_qk_norm_qknorm_amd as qk
+        self.qk, self.w = qk, w
+        x0 = to_device(inp.qkv, dev)
+        per_set = 2 * x0.numel() * x0.element_size()
+        self.n_sets = max(1, -(-ROTATE_MIN_BYTES // per_set))
+        P = inp.peer_q.shape[0]
+        self.sets = []
+        for i in range(self.n_sets):
+            x = x0 if i == 0 else x0.clone()
+            y = torch.zeros_like(x0)
+            planes = torch.empty((1 + P, 2, w.T), dtype=torch.float32, device=dev)
+            self.sets.append((x, y, planes))
+        for p in range(P):
+            pq, pk = to_device(inp.peer_q[p], dev), to_device(inp.peer_k[p], dev)
+            part = qk.qknorm_partial_stats(pq, pk, 1)
+            for s in self.sets:
+                s[2][1 + p].copy_(part[0])
+        self.gq = to_device(inp.gamma_q, dev)
+        self.gk = to_device(inp.gamma_k, dev)
+        esz = x0.element_size()
+        h = w.hq + w.hk
+        self.bytes_partial = w.T * h * esz + 8 * w.T
+        self.bytes_apply = 2 * w.T * h * esz + 8 * (1 + P) * w.T + h * esz
+        self.bytes = self.bytes_partial + self.bytes_apply
+        self.footprint = self.n_sets * per_set
+        self.launches = 2
+        self.name = "qknorm_partial_stats+qknorm_apply_with_stats"
+
+    def __call__(self, i):
+        x, y, planes = self.sets[i % self.n_sets]
+        hq, hk = self.w.hq, self.w.hk
+        self.qk.qknorm_partial_stats(x[:, :hq], x[:, hq:hq + hk], 1, planes[0:1])
+        self.qk.qknorm_apply_with_stats(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, planes,
+                                        self.w.hq_full, self.w.hk_full, y[:, :hq], y[:, hq:hq + hk])
+
+
+class CopyStep:
+    """A plain device copy of a known byte count (calibration for the
+    hardware counters and the practical bandwidth ceiling)."""
+
+    def __init__(self, nbytes, dev):
+        import torch
+        n = nbytes // 2
+        self.sets = [(torch.ones(n, dtype=torch.bfloat16, device=dev), torch.empty(n, dtype=torch.bfloat16,
+                                                                                   device=dev))
+                     for _ in range(max(1, -(-ROTATE_MIN_BYTES // (2 * nbytes))))]
+        self.n_sets = len(self.sets)
+        self.bytes = 2 * n * 2
+        self.footprint = self.n_sets * 2 * nbytes
+        self.launches = 1
+        self.name = "copy"
+
+    def __call__(self, i):
+        a, b = self.sets[i % self.n_sets]
+        b.copy_(a)
+
+
+# ----------------------------------------------------------------------------- timing
+def time_steps(step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = start.elapsed_time(end)
+    return wall, ev_ms / 1000.0
+
+
+def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
+    """The float64 oracle on the host: whole passes over the workload's tokens,
+    chunked over a thread pool, until at least `min_seconds` have passed."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    chunk = 256
+    spans = [(a, min(a + chunk, w.T)) for a in range(0, w.T, chunk)]
+
+    def work(span):
+        a, b = span
+        if w.peers:
+            planes = [oracle.qknorm_partial_stats(inp.q[a:b], inp.k[a:b], w.dtype, 1)[0]]
+            for p in range(inp.peer_q.shape[0]):
+                planes.append(oracle.qknorm_partial_stats(inp.peer_q[p, a:b], inp.peer_k[p, a:b], w.dtype, 1)[0])
+            import numpy as np
+            st = np.stack(planes).astype(np.float32)
+            oracle.qknorm_apply_with_stats(inp.q[a:b], inp.k[a:b], inp.gamma_q, inp.gamma_k, w.dtype, w.eps, st,
+                                           w.hq_full, w.hk_full)
+        else:
+            oracle.qknorm_fused(inp.q[a:b], inp.k[a:b], inp.gamma_q, inp.gamma_k, w.dtype, w.eps, w.shards[0])
+        return b - a
+
+    tokens = 0
+    passes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        while True:
+            tokens += sum(ex.map(work, spans))
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or el >= max_seconds:
+                break
+    el = time.perf_counter() - t0
+    return {
+        "value": tokens / el,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{w.key}: all {w.T} tokens x {passes} passes ({tokens} tokens, {el:.1f} s), "
+                  f"float64 NumPy oracle incl. bf16 decode and rounding, {chunk}-token chunks on {cores} threads",
+    }
+
+
+def load_traffic(workload, kernel_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_hash:
+        log(f"[bench] {path} was taken on kernel sources {d.get('kernel_source_hash')}, now {kernel_hash}: "
+            "traffic reported as null")
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--shards", type=int, default=None, help="S for the fused workloads (default: first listed)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="time a plain copy of this many bytes instead (calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by exchanging 2 float32 sums per token per rank, not implemented here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import layerwise_qk_norm_qknorm_amd as qk
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    qk.load_library()
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; library {qk.library_path()}")
+
+    if args.copy_bytes:
+        step = CopyStep(args.copy_bytes, dev)
+        wall, ev = time_steps(step, args.steps, args.warmup)
+        gbps = step.bytes / (ev / args.steps) / 1e9
+        print(json.dumps({"metric": "plain device copy", "bytes_per_launch": step.bytes,
+                          "ms_per_launch": ev / args.steps * 1e3, "GBps": gbps,
+                          "frac_of_peak": gbps / HBM_PEAK_GBPS, "steps": args.steps}), flush=True)
+        return
+
+    w = I.WORKLOADS[args.workload]
+    shards = args.shards or w.shards[0]
+    log(f"[bench] workload {w.key}: {w.title}")
+    t0 = time.perf_counter()
+    inp = I.make_inputs(w)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    if w.peers:
+        step = SplitStep(w, inp, dev)
+        plan = "; ".join(qk.describe_plan(op, w.hq, w.hk, w.T, w.dtype, 1, ld=w.ld) for op in (1, 2))
+    else:
+        step = FusedStep(w, inp, dev, shards)
+        plan = qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq)
+    torch.cuda.synchronize()
+    log(f"[bench] plan: {plan}; {step.n_sets} rotating buffer sets, {step.footprint / 2**20:.0f} MiB")
+
+    wall, ev = time_steps(step, args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    mean_launch_s = ev / args.steps
+    achieved = step.bytes / mean_launch_s / 1e9
+    log(f"[bench] {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms, "
+        f"{mean_launch_s * 1e6:.2f} us per step, {achieved:.0f} GB/s")
+
+    khash = kernel_source_hash()
+    traffic = load_traffic(w.key, khash)
+    out = {
+        "metric": "QK-Norm tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": w.T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; inputs resident in HBM, rotating buffer sets > 1 GiB)",
+        "config": {
+            "workload": w.title,
+            "key": w.key,
+            "tokens": w.T,
+            "hq": w.hq, "hk": w.hk, "hv": w.hv,
+            "layout": f"packed [{w.T}, {w.ld}]" if w.packed else "separate Q/K arrays",
+            "shards": shards,
+            "calls_per_step": step.name,
+            "out_of_place": True,
+            "rotating_sets": step.n_sets,
+            "plan": plan,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_step": step.bytes,
+            "mean_step_us": mean_launch_s * 1e6,
+            "kernel_source_hash": khash,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+        log(f"[bench] oracle: {out['cpu_baseline']['value']:.0f} tokens/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * qknorm.h -- layerwise QK-Norm on one MI355X (gfx950), as a C ABI.
+ *
+ * Library: libqknorm.so (HIP kernels for gfx950 behind plain C entry points).
+ *
+ * What is computed
+ * ----------------
+ * Source: "SwiftQK: Fast and Communication-Efficient Tensor Parallelism for
+ * Query-Key Normalization" (Kim, Han, Kim; arXiv 2608.09160v1).
+ *
+ * Layerwise QK-Norm (introduction of the paper) normalizes each token's whole
+ * projected Q vector with one RMS factor and, independently, its whole
+ * projected K vector with another, before attention; V is not touched. For one
+ * vector x of full width H, RMS-Norm (Eq. 1; its body is missing from the
+ * page text, and this library reads it as the standard RMSNorm) is
+ *
+ *     y_j = x_j * gamma_j / sqrt( (sum_i x_i^2) / H + eps ).
+ *
+ * Phase A of the paper: the only cross-shard quantity the factor needs is the
+ * plain sum of squares, so each column shard of x produces one float32
+ * partial sum and the global sum is the float32 sum of the partials. Phase B
+ * and the final scaling: each element is multiplied by gamma_j (independent
+ * of the global sum) and then by the factor r = 1/sqrt(sum/H + eps).
+ *
+ * Arithmetic (identical in every entry point, so results compose bit for bit):
+ *   - inputs are widened exactly to float32;
+ *   - partial[s] = float32 sum of x_j^2 over shard s, in a fixed order that
+ *     depends only on the shapes, the shard count and T;
+ *   - sum = ((partial[0] + partial[1]) + ...) + partial[S-1]   (float32);
+ *   - r = rsqrt(sum / H + eps)                                    (float32);
+ *   - y_j = (x_j * gamma_j) * r, rounded once to the I/O type (bf16: round
+ *     to nearest even).
+ *   The float32 accumulation is the paper's (Fig. 2(b) accumulates squared
+ *   sums in FP32 for BF16 activations); rows whose sum of squares overflows
+ *   float32 (|x| around 1e19) give 0 or NaN instead of the real result.
+ *
+ * Data layout
+ * -----------
+ * An operand describes one of Q or K as row-major rows in device memory:
+ * element (t, j) of the input is x[t * ld_x + j], 0 <= t < T, 0 <= j < h.
+ * A packed QKV buffer [T, Hq + Hk + Hv] is described by two operands with
+ * the same ld (Hq + Hk + Hv): Q at column 0, K at column Hq. V columns and
+ * any other memory are never read or written.
+ *
+ * A shard count S splits each of Q and K into S contiguous column shards of
+ * width h/S (h % S == 0 is required): shard s covers columns [s*h/S,
+ * (s+1)*h/S). This emulates one rank's view under tensor parallelism.
+ *
+ * Ownership and streams
+ * ---------------------
+ * The caller owns every buffer. The library allocates nothing and keeps no
+ * state except a per-thread error message. Work is enqueued on `stream` (a
+ * hipStream_t; NULL means the default stream) and the call returns without
+ * synchronizing. All pointers are device pointers.
+ *
+ * Errors
+ * ------
+ * Argument errors return QKNORM_ERR_INVALID_ARG before anything is launched
+ * and nothing is written; QKNORM_ERR_UNSUPPORTED means valid arguments that
+ * this library cannot run (a row wider than the kernels hold); QKNORM_ERR_HIP
+ * means a HIP runtime call failed. qknorm_last_error() gives the message.
+ * Faults inside kernels surface at the caller's next synchronization. T == 0
+ * is a no-op that returns QKNORM_OK after the scalar arguments are checked.
+ * Unaligned pointers or strides, or shard widths that are not a multiple of
+ * 16 bytes of elements, are not errors: they run a slower element-wise path
+ * with bit-identical results.
+ */
+#ifndef QKNORM_H
+#define QKNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKNORM_ABI_VERSION 1
+
+/* Largest shard count and number of statistic planes accepted. */
+#define QKNORM_MAX_SHARDS 64
+#define QKNORM_MAX_PLANES 64
+/* Largest full width H accepted by qknorm_apply_with_stats (exact in float32). */
+#define QKNORM_MAX_FULL_WIDTH (1 << 24)
+
+typedef enum qknorm_dtype {
+  QKNORM_F32 = 0,  /* float32 I/O */
+  QKNORM_BF16 = 1  /* bfloat16 I/O, float32 arithmetic */
+} qknorm_dtype_t;
+
+typedef enum qknorm_status {
+  QKNORM_OK = 0,
+  QKNORM_ERR_INVALID_ARG = 1,
+  QKNORM_ERR_UNSUPPORTED = 2,
+  QKNORM_ERR_HIP = 3
+} qknorm_status_t;
+
+/* Which entry point a plan is described for (qknorm_describe_plan). */
+typedef enum qknorm_op {
+  QKNORM_OP_FUSED = 0,
+  QKNORM_OP_PARTIAL_STATS = 1,
+  QKNORM_OP_APPLY_WITH_STATS = 2
+} qknorm_op_t;
+
+/* One of Q or K. */
+typedef struct qknorm_operand {
+  const void* x;     /* input rows, element (t, j) at x[t*ld_x + j] (elements of the I/O type) */
+  int64_t ld_x;      /* input row stride in elements, >= h */
+  void* y;           /* output rows, element (t, j) at y[t*ld_y + j]; y == x with ld_y == ld_x
+                        is in place; any other overlap with an input or output is rejected.
+                        Not used by qknorm_partial_stats (may be NULL there). */
+  int64_t ld_y;      /* output row stride in elements, >= h (ignored by qknorm_partial_stats) */
+  const void* gamma; /* h per-column scales, I/O type (not used by qknorm_partial_stats) */
+  int64_t h;         /* local width: number of columns normalized, > 0 */
+} qknorm_operand_t;
+
+/*
+ * qknorm_fused -- the whole path in one kernel: Phase A partial sums for S
+ * shards, their combination, Phase B (x * gamma) and the final scaling
+ * (Eq. 1 with H = h, the local width). Each Q/K element is read once and
+ * written once.
+ *
+ *   q, k    operand descriptors (host pointers to structs holding device pointers)
+ *   T       tokens (rows), >= 0
+ *   dtype   QKNORM_F32 or QKNORM_BF16, for x, y and gamma alike
+ *   eps     finite, >= 0
+ *   shards  S in [1, QKNORM_MAX_SHARDS]; q->h % S == 0 and k->h % S == 0
+ *   stream  hipStream_t or NULL
+ */
+int qknorm_fused(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype,
+                 float eps, int shards, void* stream);
+
+/*
+ * qknorm_partial_stats -- Phase A alone: the float32 sum of squares of every
+ * shard of every row, which is what each tensor-parallel rank would
+ * contribute to the exchange.
+ *
+ *   partials  device float32 [S][2][T]: partials[(s*2 + c)*T + t] is shard s of
+ *             Q (c = 0) or K (c = 1) for token t. Must not overlap the inputs.
+ *   other arguments as for qknorm_fused (y, ld_y and gamma are ignored).
+ */
+int qknorm_partial_stats(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T,
+                         int dtype, int shards, float* partials, void* stream);
+
+/*
+ * qknorm_apply_with_stats -- the combination and Phase B / final scaling for a
+ * local slice, given the statistic planes received from all shards: the
+ * planes are added in order p = 0 .. n_planes-1 in float32 and Eq. 1 divides
+ * by the full width (hq_full for Q, hk_full for K), not the local width.
+ *
+ *   stats     device float32 [n_planes][2][T], same layout as `partials`
+ *             (a qknorm_partial_stats output is a valid input, n_planes = S);
+ *             n_planes = 1 passes an already combined sum. Must not overlap
+ *             the outputs.
+ *   n_planes  in [1, QKNORM_MAX_PLANES]
+ *   hq_full, hk_full  full widths H, with h <= H_full <= QKNORM_MAX_FULL_WIDTH
+ *   q, k, T, dtype, eps, stream as for qknorm_fused.
+ *
+ * qknorm_fused with S shards gives bit-identical outputs to
+ * qknorm_partial_stats with S shards followed by this call with n_planes = S
+ * and H_full = h.
+ */
+int qknorm_apply_with_stats(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T,
+                            int dtype, float eps, const float* stats, int n_planes,
+                            int64_t hq_full, int64_t hk_full, void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* qknorm_last_error(void);
+
+/* QKNORM_ABI_VERSION of the built library. */
+int qknorm_abi_version(void);
+
+/*
+ * qknorm_describe_plan -- writes a one-line description of the launch the
+ * given call would make (element-wise or 16-byte path, lanes per shard,
+ * chunks per lane, waves per token) into buf (NUL-terminated, truncated to
+ * len). Validates like the call itself (op selects which one; `shards` is
+ * ignored for QKNORM_OP_APPLY_WITH_STATS) and makes no HIP call, so it works
+ * without a GPU. Device pointers are only compared, never dereferenced.
+ */
+int qknorm_describe_plan(int op, const qknorm_operand_t* q, const qknorm_operand_t* k,
+                         int64_t T, int dtype, int shards, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNORM_H */

@@ -1,0 +1,228 @@
+"""ctypes binding of libqknorm.so (argument marshalling only).
+
+The three calls keep the C names. Tensors are torch CUDA tensors used as
+device memory: each Q or K operand is a 2-D view whose columns are contiguous
+(for instance ``qkv[:, :hq]`` and ``qkv[:, hq:hq + hk]`` of a packed
+[T, Hq + Hk + Hv] buffer); its row stride becomes the C ``ld``. The work is
+enqueued on torch's current stream of the tensors' device (or on ``stream``).
+No step of the computation runs here; if the library is missing, the first
+call raises.
+"""
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqknorm.so")
+
+QKNORM_F32 = 0
+QKNORM_BF16 = 1
+QKNORM_OK = 0
+QKNORM_ERR_INVALID_ARG = 1
+QKNORM_ERR_UNSUPPORTED = 2
+QKNORM_ERR_HIP = 3
+OP_FUSED, OP_PARTIAL_STATS, OP_APPLY_WITH_STATS = 0, 1, 2
+ABI_VERSION = 1
+EXPORTS = ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats",
+           "qknorm_last_error", "qknorm_abi_version", "qknorm_describe_plan")
+
+
+class QKNormError(RuntimeError):
+    """A non-OK status from libqknorm.so; ``status`` holds the code."""
+
+    def __init__(self, status, message):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+class Operand(ctypes.Structure):
+    """qknorm_operand_t."""
+
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("ld_x", ctypes.c_int64),
+        ("y", ctypes.c_void_p),
+        ("ld_y", ctypes.c_int64),
+        ("gamma", ctypes.c_void_p),
+        ("h", ctypes.c_int64),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libqknorm.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise QKNormError(-1, f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                                  "(hipcc --offload-arch=gfx950)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER(Operand)
+        i64, vp, fl, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        lib.qknorm_fused.argtypes = [P, P, i64, ci, fl, ci, vp]
+        lib.qknorm_partial_stats.argtypes = [P, P, i64, ci, ci, vp, vp]
+        lib.qknorm_apply_with_stats.argtypes = [P, P, i64, ci, fl, vp, ci, i64, i64, vp]
+        lib.qknorm_describe_plan.argtypes = [ci, P, P, i64, ci, ci, ctypes.c_char_p, ctypes.c_size_t]
+        for fn in ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats",
+                   "qknorm_describe_plan", "qknorm_abi_version"):
+            getattr(lib, fn).restype = ci
+        lib.qknorm_last_error.restype = ctypes.c_char_p
+        lib.qknorm_last_error.argtypes = []
+        lib.qknorm_abi_version.argtypes = []
+        if lib.qknorm_abi_version() != ABI_VERSION:
+            raise QKNormError(-1, f"libqknorm.so ABI {lib.qknorm_abi_version()} != {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def abi_version():
+    return load_library().qknorm_abi_version()
+
+
+def _check(rc):
+    if rc != QKNORM_OK:
+        raise QKNormError(rc, load_library().qknorm_last_error().decode())
+
+
+# --------------------------------------------------------------------- marshalling
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return QKNORM_BF16
+    if t.dtype == torch.float32:
+        return QKNORM_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _rows(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [T, h], got {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} columns must be contiguous (stride(1) == 1)")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    # one-row (or empty) views can carry any stride(0); the row length is a valid ld
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _operand(x, y, gamma, name):
+    op = Operand()
+    op.x = x.data_ptr()
+    op.ld_x = _rows(x, name)
+    op.h = x.shape[1]
+    if y is not None:
+        if y.shape != x.shape:
+            raise ValueError(f"output for {name} has shape {tuple(y.shape)}, expected {tuple(x.shape)}")
+        op.y = y.data_ptr()
+        op.ld_y = _rows(y, f"out_{name}")
+        if y.dtype != x.dtype:
+            raise TypeError(f"output for {name} must have dtype {x.dtype}")
+    if gamma is not None:
+        if gamma.dim() != 1 or gamma.shape[0] != x.shape[1] or (gamma.shape[0] > 1 and gamma.stride(0) != 1):
+            raise ValueError(f"gamma for {name} must be contiguous [{x.shape[1]}]")
+        if gamma.dtype != x.dtype:
+            raise TypeError(f"gamma for {name} must have dtype {x.dtype}")
+        op.gamma = gamma.data_ptr()
+    return op
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _tokens(q, k):
+    if q.shape[0] != k.shape[0]:
+        raise ValueError(f"q has {q.shape[0]} rows, k has {k.shape[0]}")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must have the same dtype")
+    if q.device != k.device:
+        raise ValueError("q and k must be on the same device")
+    return q.shape[0]
+
+
+def qknorm_fused(q, k, gamma_q, gamma_k, eps, shards=1, out_q=None, out_k=None, stream=None):
+    """Layerwise QK-Norm of q [T, hq] and k [T, hk] in one kernel.
+
+    Writes ``out_q``/``out_k`` (default: in place into q and k) and returns them.
+    """
+    lib = load_library()
+    T = _tokens(q, k)
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, gamma_q, "q")
+    ok = _operand(k, out_k, gamma_k, "k")
+    _check(lib.qknorm_fused(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps),
+                            int(shards), _stream(q, stream)))
+    return out_q, out_k
+
+
+def qknorm_partial_stats(q, k, shards, partials=None, stream=None):
+    """Per-shard float32 sums of squares -> ``partials`` [S, 2, T] (allocated if None)."""
+    import torch
+    lib = load_library()
+    T = _tokens(q, k)
+    if partials is None:
+        partials = torch.empty((shards, 2, T), dtype=torch.float32, device=q.device)
+    if (partials.dtype != torch.float32 or tuple(partials.shape) != (shards, 2, T)
+            or not partials.is_contiguous()):
+        raise ValueError(f"partials must be contiguous float32 [{shards}, 2, {T}]")
+    oq = _operand(q, None, None, "q")
+    ok = _operand(k, None, None, "k")
+    _check(lib.qknorm_partial_stats(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), int(shards),
+                                    partials.data_ptr(), _stream(q, stream)))
+    return partials
+
+
+def qknorm_apply_with_stats(q, k, gamma_q, gamma_k, eps, stats, hq_full, hk_full,
+                            out_q=None, out_k=None, stream=None):
+    """Scale q/k with statistic planes ``stats`` [P, 2, T] (float32, added in order)
+    over full widths ``hq_full``/``hk_full``. Returns the outputs (default in place)."""
+    import torch
+    lib = load_library()
+    T = _tokens(q, k)
+    if stats.dim() != 3 or stats.shape[1] != 2 or stats.shape[2] != T or stats.dtype != torch.float32 \
+            or not stats.is_contiguous():
+        raise ValueError(f"stats must be contiguous float32 [P, 2, {T}]")
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, gamma_q, "q")
+    ok = _operand(k, out_k, gamma_k, "k")
+    _check(lib.qknorm_apply_with_stats(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps),
+                                       stats.data_ptr(), int(stats.shape[0]), int(hq_full), int(hk_full),
+                                       _stream(q, stream)))
+    return out_q, out_k
+
+
+def describe_plan(op, hq, hk, T, dtype="bf16", shards=1, ld=None, aligned=True):
+    """The launch a call would make, for shapes alone (no GPU needed).
+
+    Uses stand-in addresses for a packed layout (never dereferenced).
+    """
+    lib = load_library()
+    code = QKNORM_BF16 if dtype == "bf16" else QKNORM_F32
+    esz = 2 if dtype == "bf16" else 4
+    ld = ld if ld is not None else hq + hk
+    off = 0 if aligned else esz
+    if ld >= hq + hk:      # packed rows: K follows Q in the same rows
+        xq, xk = (1 << 32) + off, (1 << 32) + off + hq * esz
+    else:                  # separate arrays
+        xq, xk = (1 << 32) + off, (1 << 40) + off
+    yd = 1 << 44           # outputs and gamma far away from the inputs
+    oq = Operand(xq, ld, xq + yd, ld, (1 << 46) + off, hq)
+    ok = Operand(xk, ld, xk + yd, ld, (1 << 46) + (1 << 30) + off, hk)
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.qknorm_describe_plan(op, ctypes.byref(oq), ctypes.byref(ok), T, code, shards, buf, 512))
+    return buf.value.decode()

@@ -1,0 +1,384 @@
+// C ABI of libqknorm.so: argument validation, launch planning, error strings.
+//
+// Everything in this file is plain C++ with no HIP call, so every argument
+// error is detected (and testable) without a GPU; only qkn::launch, in
+// qknorm_kernels.hip, touches the HIP runtime.
+//
+// Source of the operation: "SwiftQK: Fast and Communication-Efficient Tensor
+// Parallelism for Query-Key Normalization" (arXiv 2608.09160v1): RMS-Norm,
+// Eq. 1; Phase A (per-shard squared sums, FP32 aggregation); Phase B and the
+// final scaling.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "qknorm.h"
+#include "qknorm_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QKNORM_OK;
+}
+
+size_t elem_size(int dtype) {
+  if (dtype == QKNORM_F32) return 4;
+  if (dtype == QKNORM_BF16) return 2;
+  return 0;
+}
+
+// The set of bytes touched by rows t < T, columns j < h of a strided matrix.
+struct Region {
+  uintptr_t base;
+  int64_t ld;   // elements
+  int64_t h;    // elements
+  int64_t T;
+  int64_t esz;  // bytes per element
+  int64_t span_bytes() const { return ((T - 1) * ld + h) * esz; }
+};
+
+// True if the two element sets may share a byte. Exact for equal strides and
+// element sizes (the packed-QKV case); conservative (byte spans) otherwise.
+bool may_overlap(const Region& a, const Region& b) {
+  if (a.T <= 0 || b.T <= 0 || a.h <= 0 || b.h <= 0) return false;
+  const uintptr_t a0 = a.base, a1 = a.base + (uintptr_t)a.span_bytes();
+  const uintptr_t b0 = b.base, b1 = b.base + (uintptr_t)b.span_bytes();
+  if (a1 <= b0 || b1 <= a0) return false;
+  if (a.ld != b.ld || a.esz != b.esz || a.T == 1 || b.T == 1) return true;
+  const int64_t d = (int64_t)(b.base - a.base);  // may be negative
+  if (d % a.esz != 0) return true;
+  const int64_t de = d / a.esz;
+  // Column of a's row grid where b's rows start.
+  const int64_t r = ((de % a.ld) + a.ld) % a.ld;
+  if (r + b.h <= a.ld) return r < a.h;                  // b occupies [r, r + b.h)
+  return true;                                          // b wraps into a's next row
+}
+
+bool same_region(const Region& a, const Region& b) {
+  return a.base == b.base && a.ld == b.ld && a.h == b.h && a.esz == b.esz;
+}
+
+bool fits(int64_t T, int64_t ld, int64_t h, int64_t esz) {
+  // (T - 1) * ld + h elements, times esz bytes, must fit in int64.
+  if (T <= 0) return true;
+  const int64_t lim = INT64_MAX / esz;
+  if (T - 1 > 0 && ld > (lim - h) / (T - 1)) return false;
+  return true;
+}
+
+struct Checked {
+  qkn::Plan plan;
+  qkn::RowArgs args;
+};
+
+const char* kName[3] = {"qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats"};
+
+// Validates the arguments shared by the three entry points and builds the
+// plan. Returns QKNORM_OK, or an error code with the message set.
+int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T,
+                   int dtype, float eps, int shards, const void* stat_buf, int n_planes,
+                   int64_t hq_full, int64_t hk_full, Checked* out, bool* noop) {
+  const char* fn = kName[mode];
+  *noop = false;
+  if (!q || !k) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k operand descriptors are required", fn);
+  const size_t esz = elem_size(dtype);
+  if (!esz) return fail(QKNORM_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (T < 0) return fail(QKNORM_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (mode != qkn::MODE_APPLY) {
+    if (shards < 1 || shards > QKNORM_MAX_SHARDS)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: shards = %d outside [1, %d]", fn, shards, QKNORM_MAX_SHARDS);
+  } else {
+    shards = 1;
+  }
+  if (mode != qkn::MODE_STATS && !(std::isfinite(eps) && eps >= 0.0f))
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  const qknorm_operand_t* ops[2] = {q, k};
+  const char* nm[2] = {"q", "k"};
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    if (o->h <= 0) return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->h = %lld must be > 0", fn, nm[c], (long long)o->h);
+    if (o->h % shards)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->h = %lld is not divisible into %d shards", fn, nm[c],
+                  (long long)o->h, shards);
+    if (o->ld_x < o->h)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->ld_x = %lld < h = %lld", fn, nm[c], (long long)o->ld_x,
+                  (long long)o->h);
+    if (mode != qkn::MODE_STATS && o->ld_y < o->h)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->ld_y = %lld < h = %lld", fn, nm[c], (long long)o->ld_y,
+                  (long long)o->h);
+    if (o->h > (int64_t)1 << 30)
+      return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s->h = %lld is too wide", fn, nm[c], (long long)o->h);
+  }
+  if (mode == qkn::MODE_APPLY) {
+    if (n_planes < 1 || n_planes > QKNORM_MAX_PLANES)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: n_planes = %d outside [1, %d]", fn, n_planes, QKNORM_MAX_PLANES);
+    if (hq_full < q->h || hk_full < k->h)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: full widths (%lld, %lld) must be >= local widths (%lld, %lld)", fn,
+                  (long long)hq_full, (long long)hk_full, (long long)q->h, (long long)k->h);
+    if (hq_full > QKNORM_MAX_FULL_WIDTH || hk_full > QKNORM_MAX_FULL_WIDTH)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: full widths must be <= %d", fn, QKNORM_MAX_FULL_WIDTH);
+  }
+  if (T == 0) {
+    *noop = true;
+    return ok();
+  }
+
+  // Pointers.
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    if (!o->x) return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->x is NULL", fn, nm[c]);
+    if (mode != qkn::MODE_STATS && (!o->y || !o->gamma))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->y and %s->gamma are required", fn, nm[c], nm[c]);
+    if (!fits(T, o->ld_x, o->h, esz) || (mode != qkn::MODE_STATS && !fits(T, o->ld_y, o->h, esz)))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s rows exceed the address range", fn, nm[c]);
+  }
+  if (mode != qkn::MODE_FUSED && !stat_buf)
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: %s buffer is NULL", fn, mode == qkn::MODE_STATS ? "partials" : "stats");
+  if (mode == qkn::MODE_STATS && T > INT64_MAX / (8 * (int64_t)shards))
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: partials size overflows", fn);
+
+  // Overlaps.
+  const int64_t e = (int64_t)esz;
+  Region xr[2], yr[2], gr[2];
+  for (int c = 0; c < 2; ++c) {
+    xr[c] = Region{(uintptr_t)ops[c]->x, ops[c]->ld_x, ops[c]->h, T, e};
+    yr[c] = Region{(uintptr_t)ops[c]->y, ops[c]->ld_y, ops[c]->h, T, e};
+    gr[c] = Region{(uintptr_t)ops[c]->gamma, ops[c]->h, ops[c]->h, 1, e};
+  }
+  if (mode != qkn::MODE_STATS) {
+    if (may_overlap(yr[0], yr[1])) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k outputs overlap", fn);
+    for (int c = 0; c < 2; ++c) {
+      if (may_overlap(yr[c], xr[1 - c]))
+        return fail(QKNORM_ERR_INVALID_ARG, "%s: %s output overlaps the %s input", fn, nm[c], nm[1 - c]);
+      if (may_overlap(yr[c], xr[c]) && !same_region(yr[c], xr[c]))
+        return fail(QKNORM_ERR_INVALID_ARG,
+                    "%s: %s output partially overlaps its input (only exact in-place is allowed)", fn, nm[c]);
+      for (int g = 0; g < 2; ++g)
+        if (may_overlap(yr[c], gr[g]))
+          return fail(QKNORM_ERR_INVALID_ARG, "%s: %s output overlaps gamma of %s", fn, nm[c], nm[g]);
+    }
+  }
+  if (mode == qkn::MODE_STATS) {
+    const Region pr{(uintptr_t)stat_buf, 1, (int64_t)shards * 2 * T, 1, 4};
+    for (int c = 0; c < 2; ++c)
+      if (may_overlap(pr, xr[c])) return fail(QKNORM_ERR_INVALID_ARG, "%s: partials overlap the %s input", fn, nm[c]);
+  }
+  if (mode == qkn::MODE_APPLY) {
+    const Region sr{(uintptr_t)stat_buf, 1, (int64_t)n_planes * 2 * T, 1, 4};
+    for (int c = 0; c < 2; ++c)
+      if (may_overlap(sr, yr[c])) return fail(QKNORM_ERR_INVALID_ARG, "%s: stats overlap the %s output", fn, nm[c]);
+  }
+
+  // Path selection: 16-byte chunks need every base 16-byte aligned, every row
+  // stride and every shard width a whole number of chunks.
+  const int vw = (int)(16 / esz);
+  bool aligned = true;
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    aligned = aligned && ((uintptr_t)o->x % 16 == 0) && (o->ld_x % vw == 0) && ((o->h / shards) % vw == 0);
+    if (mode != qkn::MODE_STATS)
+      aligned = aligned && ((uintptr_t)o->y % 16 == 0) && (o->ld_y % vw == 0) && ((uintptr_t)o->gamma % 16 == 0);
+  }
+
+  std::string why;
+  if (!qkn::make_plan(mode, dtype == QKNORM_BF16, aligned, shards, q->h, k->h, T, &out->plan, &why))
+    return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+
+  qkn::RowArgs& a = out->args;
+  std::memset(&a, 0, sizeof a);
+  a.xq = q->x;
+  a.yq = q->y;
+  a.gq = q->gamma;
+  a.ldxq = q->ld_x;
+  a.ldyq = q->ld_y;
+  a.xk = k->x;
+  a.yk = k->y;
+  a.gk = k->gamma;
+  a.ldxk = k->ld_x;
+  a.ldyk = k->ld_y;
+  a.T = T;
+  a.hq_s = out->plan.hq_s;
+  a.hk_s = out->plan.hk_s;
+  a.ncq = out->plan.ncq;
+  a.nck = out->plan.nck;
+  a.shards = out->plan.shards;
+  a.lanes = out->plan.lanes;
+  a.log2_lanes = out->plan.log2_lanes;
+  a.group = out->plan.group;
+  a.divq = (float)(mode == qkn::MODE_APPLY ? hq_full : q->h);
+  a.divk = (float)(mode == qkn::MODE_APPLY ? hk_full : k->h);
+  a.eps = eps;
+  a.partials = mode == qkn::MODE_STATS ? (float*)stat_buf : nullptr;
+  a.stats = mode == qkn::MODE_APPLY ? (const float*)stat_buf : nullptr;
+  a.n_planes = mode == qkn::MODE_APPLY ? n_planes : 0;
+  return QKNORM_OK;
+}
+
+int run(int mode, const Checked& c, void* stream) {
+  std::string err;
+  const int rc = qkn::launch(c.plan, c.args, stream, &err);
+  if (rc) return fail(QKNORM_ERR_HIP, "%s: %s", kName[mode], err.c_str());
+  return ok();
+}
+
+}  // namespace
+
+namespace qkn {
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+               Plan* p, std::string* why) {
+  Plan r;
+  r.mode = mode;
+  r.bf16 = bf16 ? 1 : 0;
+  r.aligned = aligned ? 1 : 0;
+  r.vw = bf16 ? 8 : 4;
+  r.shards = shards;
+  const int64_t hq_s = hq / shards, hk_s = hk / shards;
+  const int64_t max_chunks = (int64_t)kMaxThreads * 8;  // per token: 1024 threads x 8 slots
+  const int64_t ncq = (hq_s + r.vw - 1) / r.vw, nck = (hk_s + r.vw - 1) / r.vw;
+  if ((ncq + nck) * shards > max_chunks) {
+    *why = "rows of " + std::to_string(hq + hk) + " elements (" + std::to_string(ncq + nck) +
+           " chunks per shard x " + std::to_string(shards) + " shards) exceed the " +
+           std::to_string(max_chunks) + " chunks a block holds";
+    return false;
+  }
+  r.hq_s = (int)hq_s;
+  r.hk_s = (int)hk_s;
+  r.ncq = (int)ncq;
+  r.nck = (int)nck;
+  const int nc = r.ncq + r.nck;
+
+  // Fewest waves per token whose slot count stays <= 12 (<= 16 if nothing
+  // else fits); then, when there are too few tokens to occupy the chip,
+  // spread each token over more waves.
+  auto slots_for = [](int v) {
+    for (int s : kSlotSizes)
+      if (s >= v) return s;
+    return 0;
+  };
+  auto fits_block = [&](int l) {
+    const int g = shards * l;
+    if (g % 64 || g > kMaxThreads) return 0;
+    const int v = slots_for(ceil_div(nc, l));
+    if (!v || g > max_threads_for_slots(v)) return 0;
+    return v;
+  };
+  int best_l = 0;
+  for (int pass = 0; pass < 2 && !best_l; ++pass) {
+    const int vcap = pass == 0 ? 12 : kMaxSlots;
+    for (int l = kMinLanesPerShard; l <= kMaxThreads; l *= 2) {
+      const int v = fits_block(l);
+      if (v && v <= vcap) {
+        best_l = l;
+        break;
+      }
+    }
+  }
+  if (!best_l) {
+    *why = "no lane layout holds " + std::to_string(nc) + " chunks per shard with " + std::to_string(shards) +
+           " shards";
+    return false;
+  }
+  const int64_t busy_waves = 1024;  // waves that keep all 256 CUs fed
+  while (ceil_div(nc, best_l) >= 2 && T * (int64_t)(shards * best_l / 64) < busy_waves) {
+    if (!fits_block(best_l * 2)) break;
+    best_l *= 2;
+  }
+  r.lanes = best_l;
+  r.log2_lanes = 0;
+  while ((1 << r.log2_lanes) < best_l) ++r.log2_lanes;
+  r.group = best_l < 64 ? best_l : 64;
+  r.threads = shards * best_l;
+  r.slots = slots_for(ceil_div(nc, best_l));
+  r.waves = r.threads / 64;
+  r.lds_bytes = r.waves > 1 ? 2 * (r.threads / r.group) * 2 * (int)sizeof(float) : 0;
+  *p = r;
+  return true;
+}
+
+std::string describe(const Plan& p) {
+  char buf[256];
+  snprintf(buf, sizeof buf,
+           "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads=%d waves=%d "
+           "slots=%d lds=%d",
+           p.mode == MODE_FUSED ? "fused" : p.mode == MODE_STATS ? "partial_stats" : "apply_with_stats",
+           p.bf16 ? "bf16" : "f32", p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
+           p.lanes, p.threads, p.waves, p.slots, p.lds_bytes);
+  return buf;
+}
+
+}  // namespace qkn
+
+extern "C" {
+
+int qknorm_fused(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype, float eps,
+                 int shards, void* stream) {
+  Checked c;
+  bool noop;
+  const int rc = check_and_plan(qkn::MODE_FUSED, q, k, T, dtype, eps, shards, nullptr, 0, 0, 0, &c, &noop);
+  if (rc || noop) return rc;
+  return run(qkn::MODE_FUSED, c, stream);
+}
+
+int qknorm_partial_stats(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype, int shards,
+                         float* partials, void* stream) {
+  Checked c;
+  bool noop;
+  const int rc =
+      check_and_plan(qkn::MODE_STATS, q, k, T, dtype, 0.0f, shards, partials, 0, 0, 0, &c, &noop);
+  if (rc || noop) return rc;
+  return run(qkn::MODE_STATS, c, stream);
+}
+
+int qknorm_apply_with_stats(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype,
+                            float eps, const float* stats, int n_planes, int64_t hq_full, int64_t hk_full,
+                            void* stream) {
+  Checked c;
+  bool noop;
+  const int rc = check_and_plan(qkn::MODE_APPLY, q, k, T, dtype, eps, 1, stats, n_planes, hq_full, hk_full, &c,
+                                &noop);
+  if (rc || noop) return rc;
+  return run(qkn::MODE_APPLY, c, stream);
+}
+
+const char* qknorm_last_error(void) { return g_last_error.c_str(); }
+
+int qknorm_abi_version(void) { return QKNORM_ABI_VERSION; }
+
+int qknorm_describe_plan(int op, const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype,
+                         int shards, char* buf, size_t len) {
+  if (op < 0 || op > 2) return fail(QKNORM_ERR_INVALID_ARG, "qknorm_describe_plan: unknown op %d", op);
+  if (!buf || !len) return fail(QKNORM_ERR_INVALID_ARG, "qknorm_describe_plan: no output buffer");
+  Checked c;
+  bool noop;
+  // Stand-in statistic buffer address: only compared, never dereferenced.
+  // It sits just past the address space the operands use.
+  const void* fake = (const void*)(uintptr_t)0xFFFF000000000000ull;
+  int64_t hqf = q ? q->h : 0, hkf = k ? k->h : 0;
+  const int rc = check_and_plan(op, q, k, T, dtype, 1e-6f, shards, op == qkn::MODE_FUSED ? nullptr : fake, 1,
+                                hqf, hkf, &c, &noop);
+  if (rc) return rc;
+  const std::string s = noop ? std::string("no-op (T = 0)") : qkn::describe(c.plan);
+  snprintf(buf, len, "%s", s.c_str());
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal interface between the C ABI layer (qknorm_api.cpp: validation and
+// planning, no HIP calls) and the kernel layer (qknorm_kernels.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+namespace qkn {
+
+enum Mode : int { MODE_FUSED = 0, MODE_STATS = 1, MODE_APPLY = 2 };
+
+// Chunk-slot counts per lane that have a compiled kernel.
+constexpr int kSlotSizes[] = {1, 2, 3, 4, 6, 8, 12, 16};
+constexpr int kMaxSlots = 16;
+constexpr int kMaxThreads = 1024;   // threads working on one token (one block)
+constexpr int kMinLanesPerShard = 4;
+
+// Largest block that a kernel with `v` chunk slots per lane is compiled for.
+// Up to 8 slots the data and gamma fit the 128 VGPRs a 1024-thread block
+// allows; 12 and 16 slots need more, so those kernels take at most 256.
+constexpr int max_threads_for_slots(int v) { return v <= 8 ? kMaxThreads : 256; }
+
+// How one token's Q and K columns are spread over a block.
+//
+// Each shard's columns are cut into 16-byte chunks (8 bf16 or 4 fp32; the
+// last chunk of a shard may be partial on the element-wise path). Q shard s
+// and K shard s form one list of ncq + nck chunks, handled by a group of L
+// lanes: lane m of the group takes chunks m, m + L, m + 2L, ... (so each
+// instruction of the group touches L consecutive chunks). S groups form the
+// block of G = S * L threads, G a multiple of the 64-lane wavefront.
+struct Plan {
+  int mode = 0;
+  int bf16 = 1;       // 1: bf16 I/O, 0: fp32 I/O
+  int aligned = 0;    // 1: 16-byte loads/stores; 0: element-wise path
+  int vw = 8;         // elements per chunk
+  int shards = 1;     // S
+  int hq_s = 0;       // Q shard width (elements)
+  int hk_s = 0;       // K shard width (elements)
+  int ncq = 0;        // Q chunks per shard
+  int nck = 0;        // K chunks per shard
+  int lanes = 0;      // L, lanes per shard (power of two)
+  int log2_lanes = 0;
+  int group = 0;      // lanes per reduction group: min(L, 64)
+  int threads = 0;    // G = S * L
+  int slots = 0;      // chunk slots per lane (one of kSlotSizes)
+  int waves = 0;      // G / 64
+  int lds_bytes = 0;  // dynamic LDS for the cross-wave reduction (0 if one wave)
+};
+
+// Kernel arguments (passed by value).
+struct RowArgs {
+  const void* xq;
+  void* yq;
+  const void* gq;
+  int64_t ldxq, ldyq;
+  const void* xk;
+  void* yk;
+  const void* gk;
+  int64_t ldxk, ldyk;
+  int64_t T;
+  int hq_s, hk_s;
+  int ncq, nck;
+  int shards;
+  int lanes, log2_lanes, group;
+  float divq, divk;   // H for Q and K in Eq. 1
+  float eps;
+  float* partials;    // MODE_STATS: [S][2][T]
+  const float* stats; // MODE_APPLY: [P][2][T]
+  int n_planes;
+};
+
+// Fills `plan` for the given shapes; returns false (with a reason) if no
+// compiled kernel can hold the row.
+bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+               Plan* plan, std::string* why);
+
+std::string describe(const Plan& p);
+
+// Launches the kernel for `plan` on `stream`. Returns 0 or a HIP error code,
+// with a message in *err.
+int launch(const Plan& plan, const RowArgs& args, void* stream, std::string* err);
+
+}  // namespace qkn

@@ -1,0 +1,425 @@
+// HIP kernels for layerwise QK-Norm on gfx950 (CDNA4), and their launcher.
+//
+// Source of the operation: "SwiftQK: Fast and Communication-Efficient Tensor
+// Parallelism for Query-Key Normalization" (arXiv 2608.09160v1).
+//   - RMS-Norm, Eq. 1: y = x * gamma / sqrt(sum(x^2)/H + eps), one factor for
+//     a token's whole Q vector and one for its whole K vector (layerwise).
+//   - Phase A: per-shard squared sums, combined in FP32.
+//   - Phase B and the final scaling: x * gamma, then times the RMS factor;
+//     only the final result is written to memory.
+//
+// One kernel template serves the three entry points (MODE_FUSED,
+// MODE_STATS, MODE_APPLY) so that the per-shard sums are produced by the
+// same instructions in every mode, which is what makes the fused call and
+// the split calls agree bit for bit.
+//
+// This is a streaming, HBM-bound operation (about 1 flop per byte): there is
+// no contraction, so no MFMA. What matters is that every Q/K element is read
+// once with a 16-byte load, kept in registers through the reduction, and
+// written once with a 16-byte store, with enough loads in flight per CU.
+//
+// Work layout (see Plan in qknorm_internal.hpp): a block of G = S * L
+// threads handles one token at a time; the L lanes of shard group s own the
+// 16-byte chunks of Q shard s followed by K shard s, lane m taking chunks
+// m, m+L, m+2L, ... (`slots` of them). gamma chunks depend only on the
+// column, so each lane loads its gamma once and keeps it in registers while
+// the block walks over tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "qknorm_internal.hpp"
+
+namespace qkn {
+namespace {
+
+struct BF16 {
+  static constexpr int kVW = 8;  // elements per 16-byte chunk
+  static constexpr int kBytes = 2;
+};
+struct F32 {
+  static constexpr int kVW = 4;
+  static constexpr int kBytes = 4;
+};
+
+struct Chunk {
+  uint32_t w[4];
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Element e of a chunk as float32 (exact widening).
+template <class IO>
+__device__ __forceinline__ float elem(const Chunk& c, int e);
+template <>
+__device__ __forceinline__ float elem<BF16>(const Chunk& c, int e) {
+  const uint32_t w = c.w[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ float elem<F32>(const Chunk& c, int e) {
+  return __uint_as_float(c.w[e]);
+}
+
+// Packs float32 results into a chunk of the I/O type (bf16: round to nearest even).
+template <class IO>
+__device__ __forceinline__ void pack(Chunk& c, const float (&v)[IO::kVW]);
+template <>
+__device__ __forceinline__ void pack<BF16>(Chunk& c, const float (&v)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f32x2_t f = {v[2 * p], v[2 * p + 1]};
+    c.w[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+  }
+}
+template <>
+__device__ __forceinline__ void pack<F32>(Chunk& c, const float (&v)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) c.w[p] = __float_as_uint(v[p]);
+}
+
+// Loads `n` elements (n <= kVW) at element offset `col` of row `row`. The
+// 16-byte path requires n == kVW and a 16-byte aligned address.
+template <class IO, bool ALIGNED>
+__device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
+  Chunk c = {{0u, 0u, 0u, 0u}};
+  const char* p = row + (int64_t)col * IO::kBytes;
+  if (ALIGNED) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+    c.w[2] = v.z;
+    c.w[3] = v.w;
+  } else if (IO::kBytes == 2) {
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+    for (int e = 0; e < IO::kVW; ++e)
+      if (e < n) c.w[e >> 1] |= (uint32_t)s[e] << ((e & 1) * 16);
+  } else {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+    for (int e = 0; e < IO::kVW; ++e)
+      if (e < n) c.w[e] = s[e];
+  }
+  return c;
+}
+
+template <class IO, bool ALIGNED>
+__device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chunk& c) {
+  char* p = row + (int64_t)col * IO::kBytes;
+  if (ALIGNED) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+  } else if (IO::kBytes == 2) {
+    uint16_t* d = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+    for (int e = 0; e < IO::kVW; ++e)
+      if (e < n) d[e] = (uint16_t)(c.w[e >> 1] >> ((e & 1) * 16));
+  } else {
+    uint32_t* d = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+    for (int e = 0; e < IO::kVW; ++e)
+      if (e < n) d[e] = c.w[e];
+  }
+}
+
+// Sum of squares of one chunk, in element order (Phase A, in-lane part).
+template <class IO>
+__device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < IO::kVW; ++e) {
+    const float x = elem<IO>(c, e);
+    s = __builtin_fmaf(x, x, s);
+  }
+  return s;
+}
+
+// RMS factor of Eq. 1 for a global squared sum `ss` over full width `div`:
+// 1 / sqrt(ss / div + eps), each step correctly rounded in float32 (it runs
+// once per token, so the exact forms cost nothing measurable).
+__device__ __forceinline__ float rms_factor(float ss, float div, float eps) {
+  return 1.0f / __builtin_sqrtf(ss / div + eps);
+}
+
+// Register-pressure guard: an empty asm that claims to rewrite the four words
+// of `c`. Values the compiler decoded from them earlier (bf16 -> float32
+// widenings) can then not be kept alive across this point and are decoded
+// again where they are used, so a chunk costs 4 VGPRs instead of 8.
+__device__ __forceinline__ void keep_packed(Chunk& c) {
+  asm volatile("" : "+v"(c.w[0]), "+v"(c.w[1]), "+v"(c.w[2]), "+v"(c.w[3]));
+}
+
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+template <class IO, int V, int MODE, bool ALIGNED>
+__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const RowArgs a) {
+  extern __shared__ float red[];  // [2 buffers][groups][2]: cross-wave reduction
+  constexpr int VW = IO::kVW;
+  const int tid = threadIdx.x;
+  const int L = a.lanes;
+  const int s = tid >> a.log2_lanes;  // shard group
+  const int m = tid & (L - 1);        // lane within the group
+  const int nthreads = blockDim.x;
+
+  // Token-invariant geometry of this lane's chunk slots.
+  bool isq[V];
+  int col[V];
+  int cnt[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int u = i * L + m;
+    if (u < a.ncq) {
+      const int c = u * VW;
+      isq[i] = true;
+      col[i] = s * a.hq_s + c;
+      cnt[i] = min(VW, a.hq_s - c);
+    } else if (u < a.ncq + a.nck) {
+      const int c = (u - a.ncq) * VW;
+      isq[i] = false;
+      col[i] = s * a.hk_s + c;
+      cnt[i] = min(VW, a.hk_s - c);
+    } else {
+      isq[i] = true;
+      col[i] = 0;
+      cnt[i] = 0;
+    }
+  }
+
+  Chunk g[MODE == MODE_STATS ? 1 : V];
+  if (MODE != MODE_STATS) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      g[i] = Chunk{{0u, 0u, 0u, 0u}};
+      if (cnt[i] > 0)
+        g[i] = load_chunk<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], cnt[i]);
+    }
+  }
+
+  const int group = a.group;
+  const int ngroups = nthreads / group;
+  const int gps = L / group;  // groups per shard
+  int buf = 0;
+
+  for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
+    const char* xq_row = static_cast<const char*>(a.xq) + t * a.ldxq * IO::kBytes;
+    const char* xk_row = static_cast<const char*>(a.xk) + t * a.ldxk * IO::kBytes;
+
+    Chunk xv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      xv[i] = Chunk{{0u, 0u, 0u, 0u}};
+      if (cnt[i] > 0) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], cnt[i]);
+    }
+    if (MODE != MODE_STATS && IO::kBytes == 2) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) keep_packed(g[i]);
+    }
+
+    float ssq = 0.0f, ssk = 0.0f;
+    if (MODE != MODE_APPLY) {
+      // Phase A, in-lane: slot by slot, each chunk summed in element order.
+      float aq = 0.0f, ak = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float cs = chunk_sumsq<IO>(xv[i]);
+        aq += isq[i] ? cs : 0.0f;
+        ak += isq[i] ? 0.0f : cs;
+      }
+      // Across the lanes of a group: butterfly, every lane ends with the sum.
+      for (int off = 1; off < group; off <<= 1) {
+        aq += __shfl_xor(aq, off);
+        ak += __shfl_xor(ak, off);
+      }
+      if (nthreads == 64) {
+        // One wave per token: group s is shard s; its sum sits in lane s*L.
+        if (MODE == MODE_STATS) {
+          if (m == 0) {
+            a.partials[(int64_t)(2 * s) * a.T + t] = aq;
+            a.partials[(int64_t)(2 * s + 1) * a.T + t] = ak;
+          }
+        } else {
+          ssq = lane_read(aq, 0);
+          ssk = lane_read(ak, 0);
+          for (int j = 1; j < a.shards; ++j) {
+            ssq += lane_read(aq, j * L);
+            ssk += lane_read(ak, j * L);
+          }
+        }
+      } else {
+        // Several waves per token: group sums meet in LDS (double-buffered by
+        // token parity, so one barrier per token suffices).
+        float* rb = red + buf * ngroups * 2;
+        if ((tid & (group - 1)) == 0) {
+          rb[(tid / group) * 2 + 0] = aq;
+          rb[(tid / group) * 2 + 1] = ak;
+        }
+        __syncthreads();
+        if (MODE == MODE_STATS) {
+          if (tid < a.shards) {
+            float pq = rb[(tid * gps) * 2 + 0], pk = rb[(tid * gps) * 2 + 1];
+            for (int j = 1; j < gps; ++j) {
+              pq += rb[(tid * gps + j) * 2 + 0];
+              pk += rb[(tid * gps + j) * 2 + 1];
+            }
+            a.partials[(int64_t)(2 * tid) * a.T + t] = pq;
+            a.partials[(int64_t)(2 * tid + 1) * a.T + t] = pk;
+          }
+        } else {
+          for (int sh = 0; sh < a.shards; ++sh) {
+            float pq = rb[(sh * gps) * 2 + 0], pk = rb[(sh * gps) * 2 + 1];
+            for (int j = 1; j < gps; ++j) {
+              pq += rb[(sh * gps + j) * 2 + 0];
+              pk += rb[(sh * gps + j) * 2 + 1];
+            }
+            ssq = sh == 0 ? pq : ssq + pq;
+            ssk = sh == 0 ? pk : ssk + pk;
+          }
+        }
+        buf ^= 1;
+      }
+    } else {
+      // Statistics from outside: planes added in order (the combination step).
+      ssq = a.stats[t];
+      ssk = a.stats[a.T + t];
+      for (int p = 1; p < a.n_planes; ++p) {
+        ssq += a.stats[(int64_t)(2 * p) * a.T + t];
+        ssk += a.stats[(int64_t)(2 * p + 1) * a.T + t];
+      }
+    }
+
+    if (MODE != MODE_STATS) {
+      if (IO::kBytes == 2) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) keep_packed(xv[i]);
+      }
+      const float rq = rms_factor(ssq, a.divq, a.eps);
+      const float rk = rms_factor(ssk, a.divk, a.eps);
+      char* yq_row = static_cast<char*>(a.yq) + t * a.ldyq * IO::kBytes;
+      char* yk_row = static_cast<char*>(a.yk) + t * a.ldyk * IO::kBytes;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        if (cnt[i] > 0) {
+          const float r = isq[i] ? rq : rk;
+          float y[VW];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * r;
+          Chunk out;
+          pack<IO>(out, y);
+          store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+        }
+      }
+    }
+  }
+}
+
+using KernelFn = void (*)(const RowArgs);
+
+template <class IO, int MODE, bool ALIGNED>
+KernelFn pick_slots(int v) {
+  switch (v) {
+    case 1: return qknorm_rows<IO, 1, MODE, ALIGNED>;
+    case 2: return qknorm_rows<IO, 2, MODE, ALIGNED>;
+    case 3: return qknorm_rows<IO, 3, MODE, ALIGNED>;
+    case 4: return qknorm_rows<IO, 4, MODE, ALIGNED>;
+    case 6: return qknorm_rows<IO, 6, MODE, ALIGNED>;
+    case 8: return qknorm_rows<IO, 8, MODE, ALIGNED>;
+    case 12: return qknorm_rows<IO, 12, MODE, ALIGNED>;
+    case 16: return qknorm_rows<IO, 16, MODE, ALIGNED>;
+  }
+  return nullptr;
+}
+
+template <class IO, int MODE>
+KernelFn pick_aligned(bool aligned, int v) {
+  return aligned ? pick_slots<IO, MODE, true>(v) : pick_slots<IO, MODE, false>(v);
+}
+
+template <class IO>
+KernelFn pick_mode(int mode, bool aligned, int v) {
+  switch (mode) {
+    case MODE_FUSED: return pick_aligned<IO, MODE_FUSED>(aligned, v);
+    case MODE_STATS: return pick_aligned<IO, MODE_STATS>(aligned, v);
+    case MODE_APPLY: return pick_aligned<IO, MODE_APPLY>(aligned, v);
+  }
+  return nullptr;
+}
+
+KernelFn pick_kernel(const Plan& p) {
+  return p.bf16 ? pick_mode<BF16>(p.mode, p.aligned, p.slots) : pick_mode<F32>(p.mode, p.aligned, p.slots);
+}
+
+// Resident-block capacity per (device, kernel, block size, LDS), cached.
+std::mutex g_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, const void*, int, int>, int> g_occ;
+
+int resident_blocks(const Plan& p, KernelFn fn, int* out, std::string* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return (int)e;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto key = std::make_tuple(dev, (const void*)fn, p.threads, p.lds_bytes);
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) {
+    *out = it->second;
+    return 0;
+  }
+  int cus = 0;
+  auto ci = g_cus.find(dev);
+  if (ci == g_cus.end()) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) {
+      *err = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e);
+      return (int)e;
+    }
+    g_cus[dev] = cus;
+  } else {
+    cus = ci->second;
+  }
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), p.threads,
+                                                   (size_t)p.lds_bytes);
+  if (e != hipSuccess) {
+    *err = std::string("hipOccupancyMaxActiveBlocksPerMultiprocessor: ") + hipGetErrorString(e);
+    return (int)e;
+  }
+  if (per_cu < 1) per_cu = 1;
+  *out = per_cu * cus;
+  g_occ[key] = *out;
+  return 0;
+}
+
+}  // namespace
+
+int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
+  KernelFn fn = pick_kernel(p);
+  if (!fn) {
+    *err = "no kernel compiled for " + describe(p);
+    return (int)hipErrorInvalidValue;
+  }
+  int cap = 0;
+  int rc = resident_blocks(p, fn, &cap, err);
+  if (rc) return rc;
+  const int64_t grid = args.T < (int64_t)cap ? args.T : (int64_t)cap;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), (size_t)p.lds_bytes,
+                     static_cast<hipStream_t>(stream), args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("kernel launch: ") + hipGetErrorString(e);
+    return (int)e;
+  }
+  return 0;
+}
+
+}  // namespace qkn

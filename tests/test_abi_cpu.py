@@ -1,0 +1,193 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (stand-in device
+addresses are only compared, never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import layerwise_qk_norm_qknorm_amd as qk
+from layerwise_qk_norm_qknorm_amd.binding import (EXPORTS, OP_APPLY_WITH_STATS, OP_FUSED,
+                                                  OP_PARTIAL_STATS, Operand)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qknorm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qk.library_path()),
+                                reason="libqknorm.so not built (run __graft_entry__.build())")
+
+INVALID, UNSUPPORTED = 1, 2
+BF16, F32 = 1, 0
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qknorm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_calls():
+    assert declared_functions() == sorted(EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = qk.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qk.library_path()], capture_output=True,
+                         text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_abi_version():
+    assert qk.abi_version() == 1
+
+
+# stand-in addresses: packed rows, outputs elsewhere
+BASE, YOFF, GQ, GK, STATS = 1 << 32, 1 << 44, 1 << 46, (1 << 46) + (1 << 30), 1 << 48
+
+
+def ops(hq=256, hk=128, ld=None, esz=2, y_same=False, off=0):
+    ld = ld if ld is not None else hq + hk
+    q = Operand(BASE + off, ld, (BASE if y_same else BASE + YOFF) + off, ld, GQ, hq)
+    k = Operand(BASE + off + hq * esz, ld, (BASE if y_same else BASE + YOFF) + off + hq * esz, ld, GK, hk)
+    return q, k
+
+
+def fused(q, k, T=16, dtype=BF16, eps=1e-6, shards=1):
+    lib = qk.load_library()
+    return lib.qknorm_fused(ctypes.byref(q) if q else None, ctypes.byref(k) if k else None, T, dtype,
+                            eps, shards, None)
+
+
+def partial(q, k, T=16, dtype=BF16, shards=1, buf=STATS):
+    lib = qk.load_library()
+    return lib.qknorm_partial_stats(ctypes.byref(q), ctypes.byref(k), T, dtype, shards, buf, None)
+
+
+def apply(q, k, T=16, dtype=BF16, eps=1e-6, buf=STATS, planes=1, hqf=256, hkf=128):
+    lib = qk.load_library()
+    return lib.qknorm_apply_with_stats(ctypes.byref(q), ctypes.byref(k), T, dtype, eps, buf, planes, hqf,
+                                       hkf, None)
+
+
+def last_error():
+    return qk.load_library().qknorm_last_error().decode()
+
+
+def test_noop_when_T_is_zero():
+    q, k = ops()
+    q.x = k.x = 0  # pointers are not needed for T == 0
+    assert fused(q, k, T=0) == 0 and last_error() == ""
+    assert partial(q, k, T=0, buf=0) == 0
+    assert apply(q, k, T=0, buf=0) == 0
+
+
+@pytest.mark.parametrize("case", [
+    "null_q", "bad_dtype", "neg_T", "shards0", "shards_big", "shards_indivisible", "eps_neg", "eps_nan",
+    "eps_inf", "h0", "ld_small", "ldy_small", "null_x", "null_y", "null_gamma", "yq_overlaps_yk",
+    "yq_overlaps_xk", "partial_inplace_shift", "gamma_in_output", "huge_T",
+])
+def test_fused_rejects(case):
+    q, k = ops()
+    kw = {}
+    if case == "null_q":
+        assert fused(None, k) == INVALID
+        return
+    if case == "bad_dtype":
+        kw["dtype"] = 7
+    elif case == "neg_T":
+        kw["T"] = -1
+    elif case == "shards0":
+        kw["shards"] = 0
+    elif case == "shards_big":
+        kw["shards"] = 65
+    elif case == "shards_indivisible":
+        kw["shards"] = 3
+    elif case == "eps_neg":
+        kw["eps"] = -1e-6
+    elif case == "eps_nan":
+        kw["eps"] = float("nan")
+    elif case == "eps_inf":
+        kw["eps"] = float("inf")
+    elif case == "h0":
+        k.h = 0
+    elif case == "ld_small":
+        q.ld_x = 100
+    elif case == "ldy_small":
+        k.ld_y = 64
+    elif case == "null_x":
+        q.x = 0
+    elif case == "null_y":
+        k.y = 0
+    elif case == "null_gamma":
+        q.gamma = 0
+    elif case == "yq_overlaps_yk":
+        k.y = q.y + 100 * 2
+    elif case == "yq_overlaps_xk":
+        q.y = k.x
+        q.ld_y = q.ld_x
+    elif case == "partial_inplace_shift":
+        q.y = q.x + 2
+    elif case == "gamma_in_output":
+        q.gamma = q.y + 10 * (q.ld_y * 2)
+    elif case == "huge_T":
+        kw["T"] = 1 << 62
+    assert fused(q, k, **kw) == INVALID, case
+    assert last_error().startswith("qknorm_fused:"), last_error()
+
+
+def test_accepts_packed_in_place_and_out_of_place():
+    for y_same in (True, False):
+        q, k = ops(hq=5120, hk=1024, ld=7168, y_same=y_same)
+        buf = ctypes.create_string_buffer(256)
+        lib = qk.load_library()
+        assert lib.qknorm_describe_plan(OP_FUSED, ctypes.byref(q), ctypes.byref(k), 8192, BF16, 1, buf, 256) == 0
+
+
+def test_partial_and_apply_reject():
+    q, k = ops()
+    assert partial(q, k, buf=0) == INVALID
+    assert partial(q, k, buf=q.x) == INVALID                  # partials over the input
+    assert apply(q, k, planes=0) == INVALID
+    assert apply(q, k, planes=65) == INVALID
+    assert apply(q, k, hqf=255) == INVALID                    # full width below local width
+    assert apply(q, k, hkf=(1 << 24) + 1) == INVALID
+    assert apply(q, k, buf=0) == INVALID
+    assert apply(q, k, buf=q.y) == INVALID                    # stats over the output
+    assert apply(q, k, eps=-1.0) == INVALID
+
+
+def test_describe_plans_of_the_workloads():
+    d = qk.describe_plan(OP_FUSED, 5120, 1024, 8192, "bf16", 1, ld=7168)
+    assert "path=16B" in d and "slots=12" in d and "waves=1" in d
+    d = qk.describe_plan(OP_PARTIAL_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
+    assert "path=16B" in d and "slots=3" in d
+    d = qk.describe_plan(OP_APPLY_WITH_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
+    assert "apply_with_stats" in d
+    d = qk.describe_plan(OP_FUSED, 256, 256, 16, "f32", 2, ld=256)
+    assert "f32" in d and "shards=2" in d
+    d = qk.describe_plan(OP_FUSED, 512, 128, 16, "bf16", 1, ld=704, aligned=False)
+    assert "elementwise" in d
+    for T in (1, 8, 64, 256):
+        for S in (1, 2, 4, 8):
+            qk.describe_plan(OP_FUSED, 4096, 4096, T, "bf16", S, ld=12288)
+
+
+def test_widest_rows_and_beyond():
+    assert "slots=8" in qk.describe_plan(OP_FUSED, 57344, 8192, 4, "bf16", 1, ld=65536)
+    with pytest.raises(qk.QKNormError) as e:
+        qk.describe_plan(OP_FUSED, 65536, 8, 4, "bf16", 1, ld=65544)
+    assert e.value.status == UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qk.qknorm_fused(x[:, :32], x[:, 32:], g, g, 1e-6, 1)

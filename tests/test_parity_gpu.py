@@ -1,0 +1,386 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle,
+element by element, on the seeded synthetic workloads and on edge cases.
+
+Acceptance (written here, applied to every element):
+  * float32 I/O: |gpu - oracle| <= 1e-5 |oracle|;
+  * bf16 I/O:    the GPU bf16 result is the oracle's once-rounded bf16 result
+                 or one of its two neighbours.
+Plus bitwise properties: V columns and guard bands untouched, in place ==
+out of place, run-to-run determinism, fused == partial_stats + apply.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import layerwise_qk_norm_qknorm_amd as qk
+from layerwise_qk_norm_qknorm_amd import inputs as I
+from gpu_helpers import (DEV, Guarded, check_bf16, check_f32, fig2b_errors, np_to_torch,
+                         torch_to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qk.load_library()
+    _log(f"[gpu] {torch.cuda.get_device_name(0)} lib={qk.library_path()}")
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------- runners
+def _canvas(like, seed):
+    """Random canary bits of the shape and type of `like`."""
+    rng = np.random.default_rng(seed)
+    if like.dtype == np.uint16:
+        return rng.integers(0, 1 << 16, like.shape, dtype=np.uint32).astype(np.uint16)
+    return rng.standard_normal(like.shape).astype(np.float32)
+
+
+class Packed:
+    """Device copy of a workload's inputs in its own layout, plus an output
+    buffer of the same layout full of canary bits."""
+
+    def __init__(self, inp, seed=1, out_of_place=True):
+        w = inp.workload
+        self.w = w
+        self.inp = inp
+        if w.packed:
+            self.src = Guarded(inp.qkv, seed=seed)
+            self.dst = Guarded(_canvas(inp.qkv, seed + 100), seed=seed + 3) if out_of_place else None
+            x = self.src.view()
+            self.q, self.k = x[:, :w.hq], x[:, w.hq:w.hq + w.hk]
+            if out_of_place:
+                y = self.dst.view()
+                self.oq, self.ok = y[:, :w.hq], y[:, w.hq:w.hq + w.hk]
+            else:
+                self.oq, self.ok = self.q, self.k
+        else:
+            self.srcq, self.srck = Guarded(inp.q, seed=seed), Guarded(inp.k, seed=seed + 1)
+            self.q, self.k = self.srcq.view(), self.srck.view()
+            if out_of_place:
+                self.dstq = Guarded(np.zeros_like(inp.q), seed=seed + 2)
+                self.dstk = Guarded(np.zeros_like(inp.k), seed=seed + 3)
+                self.oq, self.ok = self.dstq.view(), self.dstk.view()
+            else:
+                self.oq, self.ok = self.q, self.k
+        self.gq = np_to_torch(inp.gamma_q).to(DEV)
+        self.gk = np_to_torch(inp.gamma_k).to(DEV)
+
+    def fused(self, shards):
+        qk.qknorm_fused(self.q, self.k, self.gq, self.gk, self.w.eps, shards, self.oq, self.ok)
+        torch.cuda.synchronize()
+        return torch_to_np(self.oq), torch_to_np(self.ok)
+
+    def untouched_outside_qk(self):
+        """V columns of the output (packed) and every guard band are unchanged."""
+        w = self.w
+        if w.packed:
+            ok = self.src.guards_intact()
+            if hasattr(self, "dst") and self.dst is not None:
+                ok = ok and self.dst.guards_intact()
+                init = self.dst.initial[self.dst.offset:self.dst.offset + self.dst.n].reshape(self.dst.shape)
+                now = self.dst.host()
+                ok = ok and np.array_equal(now[:, w.hq + w.hk:].view(np.uint8), init[:, w.hq + w.hk:].view(np.uint8))
+            # the input V columns too
+            now_in = self.src.host()
+            ok = ok and np.array_equal(now_in[:, w.hq + w.hk:], self.inp.qkv[:, w.hq + w.hk:])
+            return ok
+        bufs = [self.srcq, self.srck] + ([self.dstq, self.dstk] if hasattr(self, "dstq") else [])
+        return all(b.guards_intact() for b in bufs)
+
+
+def _compare(w, got_q, got_k, ref, what):
+    if w.dtype == "bf16":
+        eq, _ = check_bf16(got_q, ref.yq_bits, what + " Q")
+        ek, _ = check_bf16(got_k, ref.yk_bits, what + " K")
+        gq = oracle.bf16_bits_to_f64(got_q)
+        e = fig2b_errors(gq, ref.yq)
+        _log(f"[parity] {what}: exact bf16 match Q {eq:.5f} K {ek:.5f}; vs fp64 gold Q max/mean/rms "
+             f"{e[0]:.3g}/{e[1]:.3g}/{e[2]:.3g}")
+        return min(eq, ek)
+    rq = check_f32(got_q, ref.yq, what + " Q")
+    rk = check_f32(got_k, ref.yk, what + " K")
+    _log(f"[parity] {what}: max rel err Q {rq:.3g} K {rk:.3g}")
+    return None
+
+
+def _run_fused_case(w, shards, out_of_place=True):
+    _log(f"[case] fused {w.key} T={w.T} hq={w.hq} hk={w.hk} {w.dtype} S={shards} "
+         f"plan: {qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq)}")
+    inp = I.make_inputs(w)
+    dev = Packed(inp, out_of_place=out_of_place)
+    got_q, got_k = dev.fused(shards)
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, w.dtype, w.eps, shards)
+    _compare(w, got_q, got_k, ref, f"{w.key} S={shards}")
+    assert dev.untouched_outside_qk(), "write outside the Q/K columns"
+    return dev, ref
+
+
+# ----------------------------------------------------------------------- the five workloads
+def test_c1_tiny_fp32():
+    _run_fused_case(I.C1, 2)
+
+
+@pytest.mark.parametrize("shards", [1, 4])
+def test_c2_small_dense(shards):
+    _run_fused_case(I.C2, shards)
+
+
+@pytest.mark.parametrize("shards", [1, 2, 4, 8])
+@pytest.mark.parametrize("idx", range(4))
+def test_c3_decode(idx, shards):
+    _run_fused_case(I.C3[idx], shards)
+
+
+def test_c4_gqa_prefill_full_size():
+    """The bench's workload and launch configuration (out of place, S=1), every element."""
+    dev, ref = _run_fused_case(I.C4, 1)
+    assert dev.inp.meta["n_outliers"] > 40000
+
+
+def _oracle_planes(inp):
+    """Statistic planes [1 + P, 2, T] float32: this slice's sums of squares and
+    the peers' (oracle values rounded to float32), as a rank would receive them."""
+    planes = [oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", 1)[0]]
+    for p in range(inp.peer_q.shape[0]):
+        planes.append(oracle.qknorm_partial_stats(inp.peer_q[p], inp.peer_k[p], "bf16", 1)[0])
+    return np.stack(planes).astype(np.float32)
+
+
+def test_c5_rank_slice_partial_and_apply():
+    w = I.C5
+    _log(f"[case] c5 partial_stats + apply_with_stats T={w.T} local {w.hq}/{w.hk} full {w.hq_full}/{w.hk_full}")
+    inp = I.make_inputs(w)
+    dev = Packed(inp)
+    part = qk.qknorm_partial_stats(dev.q, dev.k, 1)
+    torch.cuda.synchronize()
+    got_p = part.cpu().numpy()
+    ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", 1)
+    rel = np.abs(got_p.astype(np.float64) - ref_p) / ref_p
+    _log(f"[parity] c5 partial_stats max rel err {rel.max():.3g}")
+    assert rel.max() <= 1e-5
+
+    planes = _oracle_planes(inp)
+    stats = torch.from_numpy(planes).to(DEV)
+    qk.qknorm_apply_with_stats(dev.q, dev.k, dev.gq, dev.gk, w.eps, stats, w.hq_full, w.hk_full,
+                               dev.oq, dev.ok)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "bf16", w.eps, planes,
+                                         w.hq_full, w.hk_full)
+    _compare(w, torch_to_np(dev.oq), torch_to_np(dev.ok), ref, "c5 apply 4 planes")
+    assert dev.untouched_outside_qk()
+
+
+# ----------------------------------------------------------------------- bitwise properties
+@pytest.mark.parametrize("key,shards", [("c1", 2), ("c2", 4), ("c3_t64", 8), ("c3_t1", 2), ("c3_t256", 4)])
+def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
+    w = I.WORKLOADS[key]
+    _log(f"[case] fused == split {key} S={shards}")
+    inp = I.make_inputs(w)
+    a = Packed(inp, seed=5)
+    fq, fk = a.fused(shards)
+    b = Packed(inp, seed=6)
+    part = qk.qknorm_partial_stats(b.q, b.k, shards)
+    qk.qknorm_apply_with_stats(b.q, b.k, b.gq, b.gk, w.eps, part, w.hq, w.hk, b.oq, b.ok)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_np(b.oq).view(np.uint8), fq.view(np.uint8))
+    assert np.array_equal(torch_to_np(b.ok).view(np.uint8), fk.view(np.uint8))
+    # and the partials against the oracle
+    ref = oracle.qknorm_partial_stats(inp.q, inp.k, w.dtype, shards)
+    got = part.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-5 * ref)
+
+
+@pytest.mark.parametrize("key", ["c2", "c3_t8", "c1"])
+def test_in_place_equals_out_of_place(key):
+    w = I.WORKLOADS[key]
+    inp = I.make_inputs(w)
+    s = w.shards[-1]
+    a = Packed(inp, out_of_place=True)
+    oq, ok = a.fused(s)
+    b = Packed(inp, out_of_place=False)
+    iq, ik = b.fused(s)
+    assert np.array_equal(oq.view(np.uint8), iq.view(np.uint8))
+    assert np.array_equal(ok.view(np.uint8), ik.view(np.uint8))
+    assert b.untouched_outside_qk()
+
+
+def test_run_to_run_deterministic():
+    w = I.C4.with_T(2048)
+    inp = I.make_inputs(w)
+    a = Packed(inp)
+    r1 = a.fused(1)
+    r2 = a.fused(1)
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+
+
+def test_partials_exact_on_integer_inputs():
+    """Integer-valued bf16 inputs in [-16, 16]: every float32 partial is exact,
+    so it must equal the integer sum bit for bit."""
+    rng = np.random.default_rng(21)
+    for (T, hq, hk, S) in ((37, 4096, 1024, 8), (300, 1280, 256, 1), (5, 2048, 2048, 4)):
+        xi = rng.integers(-16, 17, (T, hq + hk)).astype(np.float64)
+        w = I.Workload("int", "int", 0, T, hq, hk, 0, "bf16", False, (S,))
+        inp = I.Inputs(w, I.to_bf16_bits(xi[:, :hq]), I.to_bf16_bits(xi[:, hq:]),
+                       I.to_bf16_bits(np.ones(hq)), I.to_bf16_bits(np.ones(hk)))
+        dev = Packed(inp)
+        part = qk.qknorm_partial_stats(dev.q, dev.k, S).cpu().numpy()
+        wq, wk = hq // S, hk // S
+        for s in range(S):
+            assert np.array_equal(part[s, 0], (xi[:, s * wq:(s + 1) * wq] ** 2).sum(1).astype(np.float32))
+            assert np.array_equal(part[s, 1], (xi[:, hq + s * wk:hq + (s + 1) * wk] ** 2).sum(1).astype(np.float32))
+
+
+# ----------------------------------------------------------------------- edge cases
+def _custom_case(T, hq, hk, hv, dtype, S, seed, scale=1.0, offset=0, ld_pad=0, eps=1e-6):
+    inp = I.make_custom(T, hq, hk, hv, dtype, seed=seed, scale=scale)
+    w = inp.workload
+    _log(f"[case] custom T={T} hq={hq} hk={hk} hv={hv} {dtype} S={S} offset={offset} ld_pad={ld_pad}")
+    ld = hq + hk + hv + ld_pad
+    host = np.zeros((T, ld), dtype=inp.q.dtype)
+    host[:, :hq] = inp.q
+    host[:, hq:hq + hk] = inp.k
+    rng = np.random.default_rng(seed)
+    if hv + ld_pad:
+        host[:, hq + hk:] = rng.integers(0, 1 << 14, (T, hv + ld_pad)).astype(host.dtype)
+    src = Guarded(host, seed=seed, offset_elems=offset)
+    dst = Guarded(host, seed=seed + 1, offset_elems=offset)
+    dst_init = dst.host().copy()
+    x, y = src.view(), dst.view()
+    gq = np_to_torch(inp.gamma_q).to(DEV)
+    gk = np_to_torch(inp.gamma_k).to(DEV)
+    qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], gq, gk, eps, S, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    out = dst.host()
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, dtype, eps, S)
+    _compare(w, out[:, :hq], out[:, hq:hq + hk], ref, f"custom {hq}/{hk} S={S}")
+    assert np.array_equal(out[:, hq + hk:].view(np.uint8), dst_init[:, hq + hk:].view(np.uint8))
+    assert src.guards_intact() and dst.guards_intact()
+    assert np.array_equal(src.host(), host)
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_widths(dtype):
+    # chunk counts that do not fill a lane group or a slot: ragged tails
+    _custom_case(77, 264, 40, 24, dtype, 1, seed=31)
+    _custom_case(130, 8 * 37, 8 * 5, 0, dtype, 1, seed=32)
+    _custom_case(19, 1032, 520, 8, dtype, 2, seed=33)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_elementwise_path(dtype):
+    # misaligned base, odd row stride, shard widths not a multiple of a chunk
+    _custom_case(45, 512, 128, 64, dtype, 1, seed=41, offset=1)
+    _custom_case(33, 500, 100, 0, dtype, 1, seed=42, ld_pad=3)
+    _custom_case(29, 60, 12, 4, dtype, 3, seed=43)
+    _custom_case(17, 4100, 1030, 2, dtype, 2, seed=44, offset=3, ld_pad=1)
+
+
+def test_elementwise_path_is_bitwise_identical_to_vector_path():
+    """Same data through the 16-byte path and (shifted by one element) the
+    element-wise path: the reduction order is the same, so are the bits."""
+    a, _ = _custom_case(64, 1280, 256, 256, "bf16", 1, seed=45)
+    b, _ = _custom_case(64, 1280, 256, 256, "bf16", 1, seed=45, offset=1)
+    assert np.array_equal(a[:, :1536], b[:, :1536])
+
+
+def test_many_shards_and_widest_rows():
+    _custom_case(9, 4096, 1024, 0, "bf16", 64, seed=51)
+    _custom_case(6, 57344, 8192, 0, "bf16", 1, seed=52)       # 8192 chunks: the widest bf16 row
+    _custom_case(5, 28672, 4096, 0, "f32", 1, seed=53)        # the widest fp32 row
+    _custom_case(3, 49152, 16384, 0, "bf16", 8, seed=54)
+
+
+def test_too_wide_is_unsupported_and_writes_nothing():
+    T, hq, hk = 2, 65536, 8
+    x = torch.zeros((T, hq + hk), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(hq, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(qk.QKNormError) as e:
+        qk.qknorm_fused(x[:, :hq], x[:, hq:], g, g[:hk].clone(), 1e-6, 1)
+    assert e.value.status == 2
+
+
+def test_single_token_and_empty():
+    _custom_case(1, 5120, 1024, 1024, "bf16", 1, seed=61)
+    _custom_case(1, 256, 256, 0, "f32", 2, seed=62)
+    # T = 0: no-op, nothing written
+    x = torch.full((0, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    qk.qknorm_fused(x, x.clone(), g, g, 1e-6, 1)
+    qk.qknorm_partial_stats(x, x.clone(), 1)
+    torch.cuda.synchronize()
+
+
+def test_large_and_small_magnitudes():
+    _custom_case(40, 2048, 512, 0, "bf16", 4, seed=71, scale=1e15)
+    _custom_case(40, 2048, 512, 0, "bf16", 4, seed=72, scale=1e-15)
+    _custom_case(40, 2048, 512, 0, "f32", 2, seed=73, scale=3e8)
+
+
+def test_degenerate_rows():
+    """Zero rows give 0 with eps > 0 and NaN with eps = 0; a NaN in a row
+    makes that tensor's row NaN; an Inf gives 0 elsewhere and NaN at the Inf."""
+    T, hq, hk = 6, 256, 64
+    for dtype in ("bf16", "f32"):
+        inp = I.make_custom(T, hq, hk, 0, dtype, seed=81)
+        q, k = inp.q.copy(), inp.k.copy()
+        enc = I.to_bf16_bits if dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+        q[0] = enc(np.zeros(hq))
+        k[1] = enc(np.zeros(hk))
+        q[2, 17] = enc(np.array([np.nan]))[0] if dtype == "f32" else np.uint16(0x7FC0)
+        k[3, 5] = enc(np.array([np.inf]))[0] if dtype == "f32" else np.uint16(0x7F80)
+        for eps in (1e-6, 0.0):
+            xq = np_to_torch(q).to(DEV)
+            xk = np_to_torch(k).to(DEV)
+            gq = np_to_torch(inp.gamma_q).to(DEV)
+            gk = np_to_torch(inp.gamma_k).to(DEV)
+            qk.qknorm_fused(xq, xk, gq, gk, eps, 1)
+            torch.cuda.synchronize()
+            with np.errstate(all="ignore"):
+                ref = oracle.qknorm_fused(q, k, inp.gamma_q, inp.gamma_k, dtype, eps, 1)
+            w = inp.workload
+            _compare(w, torch_to_np(xq), torch_to_np(xk), ref, f"degenerate {dtype} eps={eps}")
+
+
+def test_argument_errors_write_nothing():
+    x = torch.randn(8, 96, device=DEV).to(torch.bfloat16)
+    before = x.clone()
+    g = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    gk = torch.ones(32, dtype=torch.bfloat16, device=DEV)
+    cases = [
+        lambda: qk.qknorm_fused(x[:, :64], x[:, 64:], g, gk, -1.0, 1),            # eps < 0
+        lambda: qk.qknorm_fused(x[:, :64], x[:, 64:], g, gk, 1e-6, 3),            # 64 % 3
+        lambda: qk.qknorm_fused(x[:, :64], x[:, 64:], g, gk, 1e-6, 1, x[:, 32:96], x[:, 64:]),  # overlap
+        lambda: qk.qknorm_apply_with_stats(x[:, :64], x[:, 64:], g, gk, 1e-6,
+                                           torch.ones(1, 2, 8, device=DEV), 32, 32),  # H_full < h
+    ]
+    for c in cases:
+        with pytest.raises(qk.QKNormError) as e:
+            c()
+        assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), before.view(torch.int16))
+
+
+def test_runs_on_the_callers_stream():
+    w = I.C3[3]
+    inp = I.make_inputs(w)
+    dev = Packed(inp)
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "bf16", w.eps, 4)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qk.qknorm_fused(dev.q, dev.k, dev.gq, dev.gk, w.eps, 4, dev.oq, dev.ok)
+    s.synchronize()
+    _compare(w, torch_to_np(dev.oq), torch_to_np(dev.ok), ref, "side stream")
