@@ -53,6 +53,7 @@ struct Chunk {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // Element e of a chunk as float32 (exact widening).
 template <class IO>
@@ -84,14 +85,20 @@ __device__ __forceinline__ void pack<F32>(Chunk& c, const float (&v)[4]) {
   for (int p = 0; p < 4; ++p) c.w[p] = __float_as_uint(v[p]);
 }
 
-// Loads `n` elements (n <= kVW) at element offset `col` of row `row`. The
-// 16-byte path requires n == kVW and a 16-byte aligned address.
+// Loads a chunk at element offset `col` of row `row`: all kVW elements on the
+// 16-byte path (which requires a 16-byte aligned address), the first `n`
+// (1 <= n <= kVW) on the element-wise path, where elements past `n` read as 0.
+//
+// Every load is unconditional: a lane whose slot is idle passes the row's
+// first chunk (always a valid address) and its value is masked by the caller.
+// Predicated loads would put each load in its own branch with a wait for it
+// before the join, leaving one load in flight per wave.
 template <class IO, bool ALIGNED>
 __device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
   Chunk c = {{0u, 0u, 0u, 0u}};
   const char* p = row + (int64_t)col * IO::kBytes;
   if (ALIGNED) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
     c.w[0] = v.x;
     c.w[1] = v.y;
     c.w[2] = v.z;
@@ -99,13 +106,17 @@ __device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
   } else if (IO::kBytes == 2) {
     const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
 #pragma unroll
-    for (int e = 0; e < IO::kVW; ++e)
-      if (e < n) c.w[e >> 1] |= (uint32_t)s[e] << ((e & 1) * 16);
+    for (int e = 0; e < IO::kVW; ++e) {
+      const uint32_t v = s[e < n ? e : 0];
+      c.w[e >> 1] |= (e < n ? v : 0u) << ((e & 1) * 16);
+    }
   } else {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
 #pragma unroll
-    for (int e = 0; e < IO::kVW; ++e)
-      if (e < n) c.w[e] = s[e];
+    for (int e = 0; e < IO::kVW; ++e) {
+      const uint32_t v = s[e < n ? e : 0];
+      c.w[e] = e < n ? v : 0u;
+    }
   }
   return c;
 }
@@ -114,7 +125,8 @@ template <class IO, bool ALIGNED>
 __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chunk& c) {
   char* p = row + (int64_t)col * IO::kBytes;
   if (ALIGNED) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+    const u32x4_t v = {c.w[0], c.w[1], c.w[2], c.w[3]};
+    *reinterpret_cast<u32x4_t*>(p) = v;
   } else if (IO::kBytes == 2) {
     uint16_t* d = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
@@ -186,7 +198,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
       isq[i] = false;
       col[i] = s * a.hk_s + c;
       cnt[i] = min(VW, a.hk_s - c);
-    } else {
+    } else {  // idle slot: reads (and ignores) the first chunk of the Q row
       isq[i] = true;
       col[i] = 0;
       cnt[i] = 0;
@@ -196,11 +208,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
   Chunk g[MODE == MODE_STATS ? 1 : V];
   if (MODE != MODE_STATS) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      g[i] = Chunk{{0u, 0u, 0u, 0u}};
-      if (cnt[i] > 0)
-        g[i] = load_chunk<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], cnt[i]);
-    }
+    for (int i = 0; i < V; ++i)
+      g[i] = load_chunk<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], max(cnt[i], 1));
   }
 
   const int group = a.group;
@@ -214,10 +223,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
 
     Chunk xv[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      xv[i] = Chunk{{0u, 0u, 0u, 0u}};
-      if (cnt[i] > 0) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], cnt[i]);
-    }
+    for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
     if (MODE != MODE_STATS && IO::kBytes == 2) {
 #pragma unroll
       for (int i = 0; i < V; ++i) keep_packed(g[i]);
@@ -229,7 +235,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
       float aq = 0.0f, ak = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const float cs = chunk_sumsq<IO>(xv[i]);
+        const float cs = cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
