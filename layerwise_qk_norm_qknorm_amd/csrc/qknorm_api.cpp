@@ -219,8 +219,9 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   a.nck = out->plan.nck;
   a.shards = out->plan.shards;
   a.lanes = out->plan.lanes;
-  a.log2_lanes = out->plan.log2_lanes;
   a.group = out->plan.group;
+  a.tok_threads = out->plan.tok_threads;
+  a.tokens_per_block = out->plan.tokens_per_block;
   a.divq = (float)(mode == qkn::MODE_APPLY ? hq_full : q->h);
   a.divk = (float)(mode == qkn::MODE_APPLY ? hk_full : k->h);
   a.eps = eps;
@@ -243,6 +244,17 @@ namespace qkn {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+static int slots_for(int v) {
+  for (int s : kSlotSizes)
+    if (s >= v) return s;
+  return 0;
+}
+
+// Launch geometry. Measured on MI355X for the packed bf16 prefill shapes:
+// what matters most is that each lane holds few chunks (about 3) so that
+// many waves share the work of a token and the loads of many tokens overlap;
+// idle slots waste issue slots, so layouts that leave more than 1/8 of the
+// slots empty are avoided when another layout fits.
 bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* p, std::string* why) {
   Plan r;
@@ -266,62 +278,60 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
   r.nck = (int)nck;
   const int nc = r.ncq + r.nck;
 
-  // Fewest waves per token whose slot count stays <= 12 (<= 16 if nothing
-  // else fits); then, when there are too few tokens to occupy the chip,
-  // spread each token over more waves.
-  auto slots_for = [](int v) {
-    for (int s : kSlotSizes)
-      if (s >= v) return s;
-    return 0;
+  // Candidate lane counts per shard: powers of two below 64 (several shards
+  // share a wave) and multiples of 64 (a shard spans whole waves).
+  struct Cand {
+    int lanes, slots;
+    int64_t waste;
   };
-  auto fits_block = [&](int l) {
+  Cand best{0, 0, 0};
+  double best_score = 1e30;
+  const bool few_tokens = T < 1024;  // under ~4 tokens per CU: favour latency
+  for (int l = kMinLanesPerShard; l <= kMaxThreads; l = l < 64 ? l * 2 : l + 64) {
     const int g = shards * l;
-    if (g % 64 || g > kMaxThreads) return 0;
+    if (g % 64 || g > kMaxThreads) continue;
     const int v = slots_for(ceil_div(nc, l));
-    if (!v || g > max_threads_for_slots(v)) return 0;
-    return v;
-  };
-  int best_l = 0;
-  for (int pass = 0; pass < 2 && !best_l; ++pass) {
-    const int vcap = pass == 0 ? 12 : kMaxSlots;
-    for (int l = kMinLanesPerShard; l <= kMaxThreads; l *= 2) {
-      const int v = fits_block(l);
-      if (v && v <= vcap) {
-        best_l = l;
-        break;
-      }
+    if (!v || g > max_threads_for_slots(v)) continue;
+    const int64_t waste = (int64_t)l * v - nc;
+    const double wfrac = (double)waste / (double)(l * v);
+    // Prefer about 3 slots per lane, few idle slots, then fewer waves; with
+    // few tokens, spread each over more waves, down to one slot per lane.
+    const double score = few_tokens
+        ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
+        : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (g / 64);
+    if (score < best_score) {
+      best_score = score;
+      best = Cand{l, v, waste};
     }
   }
-  if (!best_l) {
+  if (!best.lanes) {
     *why = "no lane layout holds " + std::to_string(nc) + " chunks per shard with " + std::to_string(shards) +
            " shards";
     return false;
   }
-  const int64_t busy_waves = 1024;  // waves that keep all 256 CUs fed
-  while (ceil_div(nc, best_l) >= 2 && T * (int64_t)(shards * best_l / 64) < busy_waves) {
-    if (!fits_block(best_l * 2)) break;
-    best_l *= 2;
-  }
-  r.lanes = best_l;
-  r.log2_lanes = 0;
-  while ((1 << r.log2_lanes) < best_l) ++r.log2_lanes;
-  r.group = best_l < 64 ? best_l : 64;
-  r.threads = shards * best_l;
-  r.slots = slots_for(ceil_div(nc, best_l));
-  r.waves = r.threads / 64;
-  r.lds_bytes = r.waves > 1 ? 2 * (r.threads / r.group) * 2 * (int)sizeof(float) : 0;
+  r.lanes = best.lanes;
+  r.slots = best.slots;
+  r.group = best.lanes < 64 ? best.lanes : 64;
+  r.tok_threads = shards * best.lanes;
+  r.waves = r.tok_threads / 64;
+  // One-wave tokens are packed four to a block; wider tokens get a block each.
+  r.tokens_per_block = (r.waves == 1 && !few_tokens) ? 4 : 1;
+  if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots)) r.tokens_per_block = 1;
+  r.threads = r.tokens_per_block * r.tok_threads;
+  const int groups_per_token = r.tok_threads / r.group;
+  r.lds_bytes = r.waves > 1 ? 2 * r.tokens_per_block * groups_per_token * 2 * (int)sizeof(float) : 0;
   *p = r;
   return true;
 }
 
 std::string describe(const Plan& p) {
-  char buf[256];
+  char buf[320];
   snprintf(buf, sizeof buf,
-           "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads=%d waves=%d "
-           "slots=%d lds=%d",
+           "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads/token=%d "
+           "tokens/block=%d waves/token=%d slots=%d lds=%d",
            p.mode == MODE_FUSED ? "fused" : p.mode == MODE_STATS ? "partial_stats" : "apply_with_stats",
            p.bf16 ? "bf16" : "f32", p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
-           p.lanes, p.threads, p.waves, p.slots, p.lds_bytes);
+           p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
   return buf;
 }
 

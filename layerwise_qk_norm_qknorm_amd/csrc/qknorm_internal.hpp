@@ -26,9 +26,11 @@ constexpr int max_threads_for_slots(int v) { return v <= 8 ? kMaxThreads : 256; 
 // Each shard's columns are cut into 16-byte chunks (8 bf16 or 4 fp32; the
 // last chunk of a shard may be partial on the element-wise path). Q shard s
 // and K shard s form one list of ncq + nck chunks, handled by a group of L
-// lanes: lane m of the group takes chunks m, m + L, m + 2L, ... (so each
-// instruction of the group touches L consecutive chunks). S groups form the
-// block of G = S * L threads, G a multiple of the 64-lane wavefront.
+// lanes: lane m of the group takes chunks m, m + L, m + 2L, ... (`slots` of
+// them), so each instruction of the group touches L consecutive chunks. S
+// groups form the G = S * L threads of one token, G a multiple of the
+// 64-lane wavefront; L is a power of two below 64 or a multiple of 64. A
+// block holds `tokens_per_block` such tokens side by side.
 struct Plan {
   int mode = 0;
   int bf16 = 1;       // 1: bf16 I/O, 0: fp32 I/O
@@ -39,13 +41,14 @@ struct Plan {
   int hk_s = 0;       // K shard width (elements)
   int ncq = 0;        // Q chunks per shard
   int nck = 0;        // K chunks per shard
-  int lanes = 0;      // L, lanes per shard (power of two)
-  int log2_lanes = 0;
-  int group = 0;      // lanes per reduction group: min(L, 64)
-  int threads = 0;    // G = S * L
+  int lanes = 0;      // L, lanes per shard
+  int group = 0;      // lanes per butterfly group: min(L, 64)
+  int tok_threads = 0;       // G = S * L
+  int tokens_per_block = 1;  // tokens handled side by side in one block
+  int threads = 0;           // block size: tokens_per_block * G
   int slots = 0;      // chunk slots per lane (one of kSlotSizes)
-  int waves = 0;      // G / 64
-  int lds_bytes = 0;  // dynamic LDS for the cross-wave reduction (0 if one wave)
+  int waves = 0;      // waves per token: G / 64
+  int lds_bytes = 0;  // dynamic LDS for the cross-wave reduction (0 if one wave per token)
 };
 
 // Kernel arguments (passed by value).
@@ -62,7 +65,7 @@ struct RowArgs {
   int hq_s, hk_s;
   int ncq, nck;
   int shards;
-  int lanes, log2_lanes, group;
+  int lanes, group, tok_threads, tokens_per_block;
   float divq, divk;   // H for Q and K in Eq. 1
   float eps;
   float* partials;    // MODE_STATS: [S][2][T]

@@ -18,20 +18,18 @@
 // once with a 16-byte load, kept in registers through the reduction, and
 // written once with a 16-byte store, with enough loads in flight per CU.
 //
-// Work layout (see Plan in qknorm_internal.hpp): a block of G = S * L
-// threads handles one token at a time; the L lanes of shard group s own the
-// 16-byte chunks of Q shard s followed by K shard s, lane m taking chunks
-// m, m+L, m+2L, ... (`slots` of them). gamma chunks depend only on the
-// column, so each lane loads its gamma once and keeps it in registers while
-// the block walks over tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...
+// Work layout (see Plan in qknorm_internal.hpp): G = S * L threads handle
+// one token; the L lanes of shard group s own the 16-byte chunks of Q shard
+// s followed by K shard s, lane m taking chunks m, m+L, m+2L, ... (`slots`
+// of them, about three). A block holds one or a few tokens side by side and
+// there is one block per such group of tokens, so many independent tokens
+// have their loads in flight on every CU; gamma is reloaded per block from
+// the caches (it is small and shared by all tokens).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <map>
-#include <mutex>
 #include <string>
-#include <tuple>
 
 #include "qknorm_internal.hpp"
 
@@ -121,12 +119,15 @@ __device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
   return c;
 }
 
+// Stores the first `n` elements of a chunk. Results are written once and not
+// read again by this kernel, so the 16-byte path marks them non-temporal
+// (streamed past the caches), which measured faster on MI355X.
 template <class IO, bool ALIGNED>
 __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chunk& c) {
   char* p = row + (int64_t)col * IO::kBytes;
   if (ALIGNED) {
     const u32x4_t v = {c.w[0], c.w[1], c.w[2], c.w[3]};
-    *reinterpret_cast<u32x4_t*>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
   } else if (IO::kBytes == 2) {
     uint16_t* d = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
@@ -173,13 +174,15 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 
 template <class IO, int V, int MODE, bool ALIGNED>
 __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const RowArgs a) {
-  extern __shared__ float red[];  // [2 buffers][groups][2]: cross-wave reduction
+  extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token][2]
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
+  const int G = a.tok_threads;
   const int L = a.lanes;
-  const int s = tid >> a.log2_lanes;  // shard group
-  const int m = tid & (L - 1);        // lane within the group
-  const int nthreads = blockDim.x;
+  const int j = tid / G;          // token slot within the block
+  const int r = tid - j * G;      // thread within the token
+  const int s = r / L;            // shard group
+  const int m = r - s * L;        // lane within the group
 
   // Token-invariant geometry of this lane's chunk slots.
   bool isq[V];
@@ -212,14 +215,21 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
       g[i] = load_chunk<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], max(cnt[i], 1));
   }
 
-  const int group = a.group;
-  const int ngroups = nthreads / group;
-  const int gps = L / group;  // groups per shard
+  const int group = a.group;            // butterfly width: min(L, 64)
+  const int gps = L / group;            // groups per shard
+  const int gpt = G / group;            // groups per token
+  const int tpb = a.tokens_per_block;
+  const int64_t step = (int64_t)gridDim.x * tpb;
   int buf = 0;
 
-  for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
-    const char* xq_row = static_cast<const char*>(a.xq) + t * a.ldxq * IO::kBytes;
-    const char* xk_row = static_cast<const char*>(a.xk) + t * a.ldxk * IO::kBytes;
+  // The loop bound is uniform over the block (barriers inside); a token slot
+  // past the end reads a valid row and writes nothing.
+  for (int64_t tb = (int64_t)blockIdx.x * tpb; tb < a.T; tb += step) {
+    const int64_t t = tb + j;
+    const bool active = t < a.T;
+    const int64_t tr = active ? t : a.T - 1;
+    const char* xq_row = static_cast<const char*>(a.xq) + tr * a.ldxq * IO::kBytes;
+    const char* xk_row = static_cast<const char*>(a.xk) + tr * a.ldxk * IO::kBytes;
 
     Chunk xv[V];
 #pragma unroll
@@ -244,46 +254,46 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
         aq += __shfl_xor(aq, off);
         ak += __shfl_xor(ak, off);
       }
-      if (nthreads == 64) {
+      if (G == 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
         if (MODE == MODE_STATS) {
-          if (m == 0) {
+          if (m == 0 && active) {
             a.partials[(int64_t)(2 * s) * a.T + t] = aq;
             a.partials[(int64_t)(2 * s + 1) * a.T + t] = ak;
           }
         } else {
           ssq = lane_read(aq, 0);
           ssk = lane_read(ak, 0);
-          for (int j = 1; j < a.shards; ++j) {
-            ssq += lane_read(aq, j * L);
-            ssk += lane_read(ak, j * L);
+          for (int sh = 1; sh < a.shards; ++sh) {
+            ssq += lane_read(aq, sh * L);
+            ssk += lane_read(ak, sh * L);
           }
         }
       } else {
-        // Several waves per token: group sums meet in LDS (double-buffered by
-        // token parity, so one barrier per token suffices).
-        float* rb = red + buf * ngroups * 2;
-        if ((tid & (group - 1)) == 0) {
-          rb[(tid / group) * 2 + 0] = aq;
-          rb[(tid / group) * 2 + 1] = ak;
+        // Several waves per token: group sums meet in LDS (double-buffered
+        // by iteration, so one barrier per iteration suffices).
+        float* rb = red + ((buf * tpb + j) * gpt) * 2;
+        if ((r & (group - 1)) == 0) {
+          rb[(r / group) * 2 + 0] = aq;
+          rb[(r / group) * 2 + 1] = ak;
         }
         __syncthreads();
         if (MODE == MODE_STATS) {
-          if (tid < a.shards) {
-            float pq = rb[(tid * gps) * 2 + 0], pk = rb[(tid * gps) * 2 + 1];
-            for (int j = 1; j < gps; ++j) {
-              pq += rb[(tid * gps + j) * 2 + 0];
-              pk += rb[(tid * gps + j) * 2 + 1];
+          if (r < a.shards && active) {
+            float pq = rb[(r * gps) * 2 + 0], pk = rb[(r * gps) * 2 + 1];
+            for (int q = 1; q < gps; ++q) {
+              pq += rb[(r * gps + q) * 2 + 0];
+              pk += rb[(r * gps + q) * 2 + 1];
             }
-            a.partials[(int64_t)(2 * tid) * a.T + t] = pq;
-            a.partials[(int64_t)(2 * tid + 1) * a.T + t] = pk;
+            a.partials[(int64_t)(2 * r) * a.T + t] = pq;
+            a.partials[(int64_t)(2 * r + 1) * a.T + t] = pk;
           }
         } else {
           for (int sh = 0; sh < a.shards; ++sh) {
             float pq = rb[(sh * gps) * 2 + 0], pk = rb[(sh * gps) * 2 + 1];
-            for (int j = 1; j < gps; ++j) {
-              pq += rb[(sh * gps + j) * 2 + 0];
-              pk += rb[(sh * gps + j) * 2 + 1];
+            for (int q = 1; q < gps; ++q) {
+              pq += rb[(sh * gps + q) * 2 + 0];
+              pk += rb[(sh * gps + q) * 2 + 1];
             }
             ssq = sh == 0 ? pq : ssq + pq;
             ssk = sh == 0 ? pk : ssk + pk;
@@ -293,15 +303,15 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
       }
     } else {
       // Statistics from outside: planes added in order (the combination step).
-      ssq = a.stats[t];
-      ssk = a.stats[a.T + t];
+      ssq = a.stats[tr];
+      ssk = a.stats[a.T + tr];
       for (int p = 1; p < a.n_planes; ++p) {
-        ssq += a.stats[(int64_t)(2 * p) * a.T + t];
-        ssk += a.stats[(int64_t)(2 * p + 1) * a.T + t];
+        ssq += a.stats[(int64_t)(2 * p) * a.T + tr];
+        ssk += a.stats[(int64_t)(2 * p + 1) * a.T + tr];
       }
     }
 
-    if (MODE != MODE_STATS) {
+    if (MODE != MODE_STATS && active) {
       if (IO::kBytes == 2) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
@@ -313,10 +323,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         if (cnt[i] > 0) {
-          const float r = isq[i] ? rq : rk;
+          const float rr = isq[i] ? rq : rk;
           float y[VW];
 #pragma unroll
-          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * r;
+          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
           Chunk out;
           pack<IO>(out, y);
           store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
@@ -327,6 +337,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
 }
 
 using KernelFn = void (*)(const RowArgs);
+
+constexpr int64_t kMaxGrid = (int64_t)1 << 30;
 
 template <class IO, int MODE, bool ALIGNED>
 KernelFn pick_slots(int v) {
@@ -362,50 +374,6 @@ KernelFn pick_kernel(const Plan& p) {
   return p.bf16 ? pick_mode<BF16>(p.mode, p.aligned, p.slots) : pick_mode<F32>(p.mode, p.aligned, p.slots);
 }
 
-// Resident-block capacity per (device, kernel, block size, LDS), cached.
-std::mutex g_mu;
-std::map<int, int> g_cus;
-std::map<std::tuple<int, const void*, int, int>, int> g_occ;
-
-int resident_blocks(const Plan& p, KernelFn fn, int* out, std::string* err) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    *err = std::string("hipGetDevice: ") + hipGetErrorString(e);
-    return (int)e;
-  }
-  std::lock_guard<std::mutex> lk(g_mu);
-  auto key = std::make_tuple(dev, (const void*)fn, p.threads, p.lds_bytes);
-  auto it = g_occ.find(key);
-  if (it != g_occ.end()) {
-    *out = it->second;
-    return 0;
-  }
-  int cus = 0;
-  auto ci = g_cus.find(dev);
-  if (ci == g_cus.end()) {
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) {
-      *err = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e);
-      return (int)e;
-    }
-    g_cus[dev] = cus;
-  } else {
-    cus = ci->second;
-  }
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), p.threads,
-                                                   (size_t)p.lds_bytes);
-  if (e != hipSuccess) {
-    *err = std::string("hipOccupancyMaxActiveBlocksPerMultiprocessor: ") + hipGetErrorString(e);
-    return (int)e;
-  }
-  if (per_cu < 1) per_cu = 1;
-  *out = per_cu * cus;
-  g_occ[key] = *out;
-  return 0;
-}
-
 }  // namespace
 
 int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
@@ -414,10 +382,10 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
     *err = "no kernel compiled for " + describe(p);
     return (int)hipErrorInvalidValue;
   }
-  int cap = 0;
-  int rc = resident_blocks(p, fn, &cap, err);
-  if (rc) return rc;
-  const int64_t grid = args.T < (int64_t)cap ? args.T : (int64_t)cap;
+  // One block per tokens_per_block tokens; the kernel's token loop covers
+  // any remainder beyond the largest grid.
+  const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
+  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), (size_t)p.lds_bytes,
                      static_cast<hipStream_t>(stream), args);
   const hipError_t e = hipGetLastError();

@@ -163,10 +163,15 @@ def test_partial_and_apply_reject():
 
 
 def test_describe_plans_of_the_workloads():
+    # GQA prefill: 768 chunks per token over 256 lanes, 3 each, one token per block
     d = qk.describe_plan(OP_FUSED, 5120, 1024, 8192, "bf16", 1, ld=7168)
-    assert "path=16B" in d and "slots=12" in d and "waves=1" in d
+    assert "path=16B" in d and "slots=3" in d and "waves/token=4" in d and "tokens/block=1" in d
+    # rank slice: 192 chunks over one wave, 3 each, four tokens per block
     d = qk.describe_plan(OP_PARTIAL_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
-    assert "path=16B" in d and "slots=3" in d
+    assert "path=16B" in d and "slots=3" in d and "waves/token=1" in d and "tokens/block=4" in d
+    # a single decode token is spread over 16 waves, one chunk per lane
+    d = qk.describe_plan(OP_FUSED, 4096, 4096, 1, "bf16", 1, ld=12288)
+    assert "slots=1" in d and "waves/token=16" in d
     d = qk.describe_plan(OP_APPLY_WITH_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
     assert "apply_with_stats" in d
     d = qk.describe_plan(OP_FUSED, 256, 256, 16, "f32", 2, ld=256)
