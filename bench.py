@@ -1,6 +1,6 @@
 """Benchmark of the layerwise QK-Norm hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c4|c5|c2|c3_t1|...]
+    python bench.py [--steps K] [--warmup W] [--workload gqa_prefill|rank_slice|small_dense|decode_t1|...]
 
 A step is one pass of the whole path over one batch: for the default
 workload (GQA prefill: T = 8192 tokens, Q 5120 + K 1024 columns normalized,
@@ -182,14 +182,18 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
     chunk = 256
     spans = [(a, min(a + chunk, w.T)) for a in range(0, w.T, chunk)]
 
+    peer_planes = None
+    if w.peers:  # received planes: prepared before timing, as on the GPU side
+        import numpy as np
+        peer_planes = np.stack([oracle.qknorm_partial_stats(inp.peer_q[p], inp.peer_k[p], w.dtype, 1)[0]
+                                for p in range(inp.peer_q.shape[0])]).astype(np.float32)
+
     def work(span):
         a, b = span
         if w.peers:
-            planes = [oracle.qknorm_partial_stats(inp.q[a:b], inp.k[a:b], w.dtype, 1)[0]]
-            for p in range(inp.peer_q.shape[0]):
-                planes.append(oracle.qknorm_partial_stats(inp.peer_q[p, a:b], inp.peer_k[p, a:b], w.dtype, 1)[0])
             import numpy as np
-            st = np.stack(planes).astype(np.float32)
+            local = oracle.qknorm_partial_stats(inp.q[a:b], inp.k[a:b], w.dtype, 1).astype(np.float32)
+            st = np.concatenate([local, peer_planes[:, :, a:b]])
             oracle.qknorm_apply_with_stats(inp.q[a:b], inp.k[a:b], inp.gamma_q, inp.gamma_k, w.dtype, w.eps, st,
                                            w.hq_full, w.hk_full)
         else:
@@ -232,17 +236,87 @@ def load_traffic(workload, kernel_hash):
     return d.get("traffic_bytes_per_launch")
 
 
+def _counter_rows(directory, counter):
+    """(kernel name, value) for every dispatch in the counter CSVs under `directory`."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    return rows
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else None
+
+
+def record_traffic(workload, d_fetch, d_write, d_copy_fetch, d_copy_write, copy_bytes, commands):
+    """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, for the
+    kernel and for a plain copy of `copy_bytes`) into HBM bytes per launch,
+    stored with the hash of the kernel sources they were taken on."""
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+    med = {}
+    for key, d, ctr, pat in (("fetch", d_fetch, "FETCH_SIZE", "qknorm_rows"),
+                             ("write", d_write, "WRITE_SIZE", "qknorm_rows"),
+                             ("copy_fetch", d_copy_fetch, "FETCH_SIZE", "copy"),
+                             ("copy_write", d_copy_write, "WRITE_SIZE", "copy")):
+        vals = [v for n, v in _counter_rows(d, ctr) if pat in n]
+        if key.startswith("copy"):  # the timed copies, not set-up traffic
+            top = max(vals)
+            vals = [v for v in vals if v > 0.5 * top]
+        med[key] = _median(vals)
+        log(f"[traffic] {key}: {len(vals)} dispatches, median {med[key]} KiB")
+    f_scale = copy_bytes / (med["copy_fetch"] * 1024.0)
+    w_scale = copy_bytes / (med["copy_write"] * 1024.0)
+    w = I.WORKLOADS[workload]
+    esz = 2 if w.dtype == "bf16" else 4
+    algo = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+    traffic = med["fetch"] * 1024.0 * f_scale + med["write"] * 1024.0 * w_scale
+    out = {
+        "workload": workload,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": med["fetch"],
+        "write_kib_per_dispatch": med["write"],
+        "copy_known_bytes": copy_bytes,
+        "copy_fetch_kib": med["copy_fetch"],
+        "copy_write_kib": med["copy_write"],
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": traffic / algo,
+        "commands": commands,
+    }
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--workload", default="gqa_prefill")
     ap.add_argument("--shards", type=int, default=None, help="S for the fused workloads (default: first listed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain copy of this many bytes instead (calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output (no GPU needed)")
+    ap.add_argument("--traffic-copy-bytes", type=int, default=100663296)
+    ap.add_argument("--traffic-commands", default="", help="the rocprofv3 commands, recorded with the result")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, args.traffic_copy_bytes,
+                       [c for c in args.traffic_commands.split(";;") if c])
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

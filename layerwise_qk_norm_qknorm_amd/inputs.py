@@ -61,20 +61,20 @@ class Workload:
         return replace(self, T=T)
 
 
-C1 = Workload("c1", "Tiny: fp32, separate Q/K [16,256], S=2", 1, 16, 256, 256, 0, "f32", False,
+TINY = Workload("tiny", "Tiny: fp32, separate Q/K [16,256], S=2", 1, 16, 256, 256, 0, "f32", False,
               (2,), gamma_dist="uniform_0.5_1.5")
-C2 = Workload("c2", "Small dense: bf16 packed [512, 3*2048], per-token LogNormal scale", 2, 512,
+SMALL_DENSE = Workload("small_dense", "Small dense: bf16 packed [512, 3*2048], per-token LogNormal scale", 2, 512,
               2048, 2048, 2048, "bf16", True, (1, 4), x_dist="normal_token_scale")
-C3 = tuple(
-    Workload(f"c3_t{T}", f"Decode-shaped: T={T}, bf16 packed [T, 12288]", 30 + i, T, 4096, 4096,
+DECODE = tuple(
+    Workload(f"decode_t{T}", f"Decode-shaped: T={T}, bf16 packed [T, 12288]", 30 + i, T, 4096, 4096,
              4096, "bf16", True, (1, 2, 4, 8))
     for i, T in enumerate((1, 8, 64, 256)))
-C4 = Workload("c4", "GQA prefill: T=8192, bf16 packed [8192, 7168], 0.1% outliers x50, S=1", 4,
+GQA_PREFILL = Workload("gqa_prefill", "GQA prefill: T=8192, bf16 packed [8192, 7168], 0.1% outliers x50, S=1", 4,
               8192, 5120, 1024, 1024, "bf16", True, (1,), x_dist="normal_outliers")
-C5 = Workload("c5", "Rank slice: T=16384, local 1280/256 of 5120/1024, bf16 packed [16384, 1792]",
+RANK_SLICE = Workload("rank_slice", "Rank slice: T=16384, local 1280/256 of 5120/1024, bf16 packed [16384, 1792]",
               5, 16384, 1280, 256, 256, "bf16", True, (1,), hq_full=5120, hk_full=1024, peers=3)
 
-WORKLOADS = {w.key: w for w in (C1, C2, *C3, C4, C5)}
+WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE)}
 
 
 def _rng(cfg_id, stream):

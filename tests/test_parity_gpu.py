@@ -128,24 +128,24 @@ def _run_fused_case(w, shards, out_of_place=True):
 
 
 # ----------------------------------------------------------------------- the five workloads
-def test_c1_tiny_fp32():
-    _run_fused_case(I.C1, 2)
+def test_tiny_fp32():
+    _run_fused_case(I.TINY, 2)
 
 
 @pytest.mark.parametrize("shards", [1, 4])
-def test_c2_small_dense(shards):
-    _run_fused_case(I.C2, shards)
+def test_small_dense(shards):
+    _run_fused_case(I.SMALL_DENSE, shards)
 
 
 @pytest.mark.parametrize("shards", [1, 2, 4, 8])
 @pytest.mark.parametrize("idx", range(4))
-def test_c3_decode(idx, shards):
-    _run_fused_case(I.C3[idx], shards)
+def test_decode(idx, shards):
+    _run_fused_case(I.DECODE[idx], shards)
 
 
-def test_c4_gqa_prefill_full_size():
+def test_gqa_prefill_full_size():
     """The bench's workload and launch configuration (out of place, S=1), every element."""
-    dev, ref = _run_fused_case(I.C4, 1)
+    dev, ref = _run_fused_case(I.GQA_PREFILL, 1)
     assert dev.inp.meta["n_outliers"] > 40000
 
 
@@ -158,9 +158,9 @@ def _oracle_planes(inp):
     return np.stack(planes).astype(np.float32)
 
 
-def test_c5_rank_slice_partial_and_apply():
-    w = I.C5
-    _log(f"[case] c5 partial_stats + apply_with_stats T={w.T} local {w.hq}/{w.hk} full {w.hq_full}/{w.hk_full}")
+def test_rank_slice_partial_and_apply():
+    w = I.RANK_SLICE
+    _log(f"[case] rank_slice partial_stats + apply_with_stats T={w.T} local {w.hq}/{w.hk} full {w.hq_full}/{w.hk_full}")
     inp = I.make_inputs(w)
     dev = Packed(inp)
     part = qk.qknorm_partial_stats(dev.q, dev.k, 1)
@@ -168,7 +168,7 @@ def test_c5_rank_slice_partial_and_apply():
     got_p = part.cpu().numpy()
     ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", 1)
     rel = np.abs(got_p.astype(np.float64) - ref_p) / ref_p
-    _log(f"[parity] c5 partial_stats max rel err {rel.max():.3g}")
+    _log(f"[parity] rank_slice partial_stats max rel err {rel.max():.3g}")
     assert rel.max() <= 1e-5
 
     planes = _oracle_planes(inp)
@@ -178,12 +178,12 @@ def test_c5_rank_slice_partial_and_apply():
     torch.cuda.synchronize()
     ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "bf16", w.eps, planes,
                                          w.hq_full, w.hk_full)
-    _compare(w, torch_to_np(dev.oq), torch_to_np(dev.ok), ref, "c5 apply 4 planes")
+    _compare(w, torch_to_np(dev.oq), torch_to_np(dev.ok), ref, "rank_slice apply 4 planes")
     assert dev.untouched_outside_qk()
 
 
 # ----------------------------------------------------------------------- bitwise properties
-@pytest.mark.parametrize("key,shards", [("c1", 2), ("c2", 4), ("c3_t64", 8), ("c3_t1", 2), ("c3_t256", 4)])
+@pytest.mark.parametrize("key,shards", [("tiny", 2), ("small_dense", 4), ("decode_t64", 8), ("decode_t1", 2), ("decode_t256", 4)])
 def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
     w = I.WORKLOADS[key]
     _log(f"[case] fused == split {key} S={shards}")
@@ -202,7 +202,7 @@ def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
     assert np.all(np.abs(got - ref) <= 1e-5 * ref)
 
 
-@pytest.mark.parametrize("key", ["c2", "c3_t8", "c1"])
+@pytest.mark.parametrize("key", ["small_dense", "decode_t8", "tiny"])
 def test_in_place_equals_out_of_place(key):
     w = I.WORKLOADS[key]
     inp = I.make_inputs(w)
@@ -217,7 +217,7 @@ def test_in_place_equals_out_of_place(key):
 
 
 def test_run_to_run_deterministic():
-    w = I.C4.with_T(2048)
+    w = I.GQA_PREFILL.with_T(2048)
     inp = I.make_inputs(w)
     a = Packed(inp)
     r1 = a.fused(1)
@@ -375,7 +375,7 @@ def test_argument_errors_write_nothing():
 
 
 def test_runs_on_the_callers_stream():
-    w = I.C3[3]
+    w = I.DECODE[3]
     inp = I.make_inputs(w)
     dev = Packed(inp)
     ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "bf16", w.eps, 4)
