@@ -297,6 +297,63 @@ def record_traffic(workload, d_fetch, d_write, d_copy_fetch, d_copy_write, copy_
     print(json.dumps(out), flush=True)
 
 
+def latency_table(dev, reps=200):
+    """Per-call times of the small, launch- and latency-bound workloads:
+    median of single calls bracketed by HIP events, and the mean over
+    back-to-back calls (buffers stay cache resident at these sizes)."""
+    import torch
+    import layerwise_qk_norm_qknorm_amd as qk
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+
+    rows = []
+    cases = [(I.TINY, s) for s in I.TINY.shards] + [(I.SMALL_DENSE, s) for s in I.SMALL_DENSE.shards]
+    cases += [(w, s) for w in I.DECODE for s in w.shards]
+    for w, shards in cases:
+        inp = I.make_inputs(w)
+        if w.packed:
+            x = to_device(inp.qkv, dev)
+            y = torch.zeros_like(x)
+            args = (x[:, :w.hq], x[:, w.hq:w.hq + w.hk])
+            outs = (y[:, :w.hq], y[:, w.hq:w.hq + w.hk])
+        else:
+            args = (to_device(inp.q, dev), to_device(inp.k, dev))
+            outs = (torch.zeros_like(args[0]), torch.zeros_like(args[1]))
+        gq, gk = to_device(inp.gamma_q, dev), to_device(inp.gamma_k, dev)
+
+        def call():
+            qk.qknorm_fused(*args, gq, gk, w.eps, shards, *outs)
+
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        single = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            b.synchronize()
+            single.append(a.elapsed_time(b) * 1e3)
+        single.sort()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        b.synchronize()
+        esz = 2 if w.dtype == "bf16" else 4
+        nbytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+        row = {"workload": w.key, "tokens": w.T, "shards": shards,
+               "plan": qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq),
+               "single_call_us_p10": single[reps // 10], "single_call_us_median": single[reps // 2],
+               "single_call_us_p90": single[(9 * reps) // 10],
+               "back_to_back_us": a.elapsed_time(b) * 1e3 / reps, "bytes": nbytes}
+        row["GBps_back_to_back"] = nbytes / (row["back_to_back_us"] * 1e-6) / 1e9
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +367,8 @@ def main():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output (no GPU needed)")
     ap.add_argument("--traffic-copy-bytes", type=int, default=100663296)
+    ap.add_argument("--latency", action="store_true",
+                    help="per-call times of the tiny, small-dense and decode workloads (one JSON line each)")
     ap.add_argument("--traffic-commands", default="", help="the rocprofv3 commands, recorded with the result")
     args = ap.parse_args()
 
@@ -335,6 +394,10 @@ def main():
     dev = "cuda:0"
     qk.load_library()
     log(f"[bench] device {torch.cuda.get_device_name(0)}; library {qk.library_path()}")
+
+    if args.latency:
+        latency_table(dev)
+        return
 
     if args.copy_bytes:
         step = CopyStep(args.copy_bytes, dev)

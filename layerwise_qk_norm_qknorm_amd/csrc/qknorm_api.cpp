@@ -287,11 +287,17 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
   Cand best{0, 0, 0};
   double best_score = 1e30;
   const bool few_tokens = T < 1024;  // under ~4 tokens per CU: favour latency
-  for (int l = kMinLanesPerShard; l <= kMaxThreads; l = l < 64 ? l * 2 : l + 64) {
+  // Slots per lane for `l` lanes per shard, or 0 if that layout does not fit a block.
+  auto fits_block = [&](int l) {
     const int g = shards * l;
-    if (g % 64 || g > kMaxThreads) continue;
+    if (g % 64 || g > kMaxThreads) return 0;
     const int v = slots_for(ceil_div(nc, l));
-    if (!v || g > max_threads_for_slots(v)) continue;
+    return (v && g <= max_threads_for_slots(v)) ? v : 0;
+  };
+  for (int l = kMinLanesPerShard; l <= kMaxThreads; l = l < 64 ? l * 2 : l + 64) {
+    const int v = fits_block(l);
+    if (!v) continue;
+    const int g = shards * l;
     const int64_t waste = (int64_t)l * v - nc;
     const double wfrac = (double)waste / (double)(l * v);
     // Prefer about 3 slots per lane, few idle slots, then fewer waves; with

@@ -168,6 +168,28 @@ __device__ __forceinline__ void keep_packed(Chunk& c) {
   asm volatile("" : "+v"(c.w[0]), "+v"(c.w[1]), "+v"(c.w[2]), "+v"(c.w[3]));
 }
 
+// Sum over aligned groups of `group` lanes (a power of two, 4..64); every
+// lane of a group ends with the same value. Inside a 16-lane row the steps
+// are DPP moves fused into the adds (quad permutes, then the half-row and
+// row mirrors, which pair lanes of the two halves once each half is
+// uniform); only the 16- and 32-lane steps cross rows through the LDS
+// crossbar. Each step adds two lanes' values, a + b on one and b + a on the
+// other, so all lanes of a group hold bitwise the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float group_sum(float v, int group) {
+  v += dpp_move<0xB1>(v);                   // lanes i ^ 1   (quad_perm 1,0,3,2)
+  if (group > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
+  if (group > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
+  if (group > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
+  if (group > 16) v += __shfl_xor(v, 16);
+  if (group > 32) v += __shfl_xor(v, 32);
+  return v;
+}
+
 __device__ __forceinline__ float lane_read(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -249,11 +271,9 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
-      // Across the lanes of a group: butterfly, every lane ends with the sum.
-      for (int off = 1; off < group; off <<= 1) {
-        aq += __shfl_xor(aq, off);
-        ak += __shfl_xor(ak, off);
-      }
+      // Across the lanes of a group: every lane ends with the group's sum.
+      aq = group_sum(aq, group);
+      ak = group_sum(ak, group);
       if (G == 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
         if (MODE == MODE_STATS) {
