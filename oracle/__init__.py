@@ -19,6 +19,9 @@ page of the paper.
   global statistic is the sum of those partial sums.
 * Phase B and the final scaling: the shard is multiplied by gamma and then by
   the global RMS factor.
+* Introduction: headwise QK-Norm (an extension beyond the layerwise path)
+  computes an independent factor per attention head: Eq. 1 applied to every
+  head vector with H = head_dim.
 * Fig. 2(b): the precision study compares against an FP64 RMSNorm over the
   full vector, which is what this oracle is (every step in float64).
 
@@ -42,4 +45,6 @@ from .qknorm import (  # noqa: F401
     qknorm_fused,
     qknorm_partial_stats,
     qknorm_apply_with_stats,
+    headwise_rmsnorm,
+    qknorm_headwise,
 )

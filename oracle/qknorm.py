@@ -115,8 +115,31 @@ def apply_with_stats(x, gamma, planes, h_full, eps):
     return scale_rows(x, gamma, denom)
 
 
+def headwise_rmsnorm(x, gamma, eps, head_dim, gamma_head_stride):
+    """Headwise QK-Norm: every head (head_dim contiguous columns) of every row
+    is its own vector for Eq. 1, with H = head_dim and its own factor.
+
+    The paper's introduction defines the headwise granularity as one
+    independent normalization factor per attention head. gamma element
+    (head, j) is gamma[head * gamma_head_stride + j]: stride 0 shares one
+    [head_dim] vector across heads, stride head_dim gives every column its
+    own scale.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    T, h = x.shape
+    if head_dim < 1 or h % head_dim:
+        raise ValueError(f"width {h} is not a whole number of heads of {head_dim}")
+    y = np.empty_like(x)
+    for head in range(h // head_dim):
+        cols = slice(head * head_dim, (head + 1) * head_dim)
+        g0 = head * gamma_head_stride
+        y[:, cols], _ = layerwise_rmsnorm(x[:, cols], gamma[g0:g0 + head_dim], eps, 1)
+    return y
+
+
 # --------------------------------------------------------------------------
-# the three calls of the library, on the same inputs the library receives
+# the calls of the library, on the same inputs the library receives
 # --------------------------------------------------------------------------
 class QKResult:
     """Oracle outputs for one call.
@@ -169,4 +192,12 @@ def qknorm_apply_with_stats(xq, xk, gamma_q, gamma_k, dtype, eps, stats, hq_full
     st = np.asarray(stats, dtype=np.float32).astype(np.float64)
     yq = apply_with_stats(decode_input(xq, dtype), decode_input(gamma_q, dtype), st[:, 0, :], hq_full, e)
     yk = apply_with_stats(decode_input(xk, dtype), decode_input(gamma_k, dtype), st[:, 1, :], hk_full, e)
+    return QKResult(yq, yk, dtype)
+
+
+def qknorm_headwise(xq, xk, gamma_q, gamma_k, dtype, eps, head_dim, gamma_head_stride):
+    """Headwise QK-Norm of Q rows and, separately, K rows (heads of head_dim)."""
+    e = eps_as_passed(eps)
+    yq = headwise_rmsnorm(decode_input(xq, dtype), decode_input(gamma_q, dtype), e, head_dim, gamma_head_stride)
+    yk = headwise_rmsnorm(decode_input(xk, dtype), decode_input(gamma_k, dtype), e, head_dim, gamma_head_stride)
     return QKResult(yq, yk, dtype)

@@ -293,6 +293,71 @@ def pin_nonfinite_and_zero_rows():
         assert y[0, 0] == 0 and np.isnan(y[0, 1]) and y[0, 2] == 0 and y[0, 3] == 0
 
 
+# ---------------------------------------------------------------- headwise QK-Norm
+def pin_headwise_one_head_is_layerwise():
+    """A single head spanning the row is layerwise RMS-Norm."""
+    rng = _rng(12)
+    x = rng.standard_normal((5, 96))
+    g = rng.normal(1, 0.1, 96)
+    for stride in (0, 96):
+        _close(oq.headwise_rmsnorm(x, g, 1e-6, 96, stride), oq.layerwise_rmsnorm(x, g, 1e-6)[0], rel=1e-15)
+
+
+def pin_headwise_torch_rms_norm_fp64():
+    """[T, heads, head_dim] RMS-Norm over the last dim (torch, fp64): a shared
+    [head_dim] weight is stride 0; a per-column weight is stride head_dim."""
+    rng = _rng(13)
+    T, nh, hd = 7, 6, 40
+    x = rng.standard_normal((T, nh * hd)) * rng.lognormal(0, 1, (T, 1))
+    xt = torch.from_numpy(x).view(T, nh, hd)
+    g_shared = rng.normal(1, 0.2, hd)
+    ref = torch.nn.functional.rms_norm(xt, [hd], torch.from_numpy(g_shared), 1e-6).reshape(T, -1).numpy()
+    _close(oq.headwise_rmsnorm(x, g_shared, 1e-6, hd, 0), ref, rel=1e-14)
+    g_full = rng.normal(1, 0.2, nh * hd)
+    ref = (torch.nn.functional.rms_norm(xt, [hd], None, 1e-6).reshape(T, -1) * torch.from_numpy(g_full)).numpy()
+    _close(oq.headwise_rmsnorm(x, g_full, 1e-6, hd, hd), ref, rel=1e-14)
+
+
+def pin_headwise_constant_heads():
+    """Head h constant c_h: y = c_h / sqrt(c_h^2 + eps) * gamma, per head."""
+    hd, cs = 16, (3.0, -0.5, 7.0, 1e-3)
+    x = np.concatenate([np.full((2, hd), c) for c in cs], axis=1)
+    g = np.linspace(0.5, 1.5, hd)
+    y = oq.headwise_rmsnorm(x, g, 0.25, hd, 0)
+    for i, c in enumerate(cs):
+        _close(y[:, i * hd:(i + 1) * hd], np.tile(c / math.sqrt(c * c + 0.25) * g, (2, 1)), rel=1e-14)
+
+
+def pin_headwise_heads_independent():
+    """Changing one head changes no other head's result (bit for bit)."""
+    rng = _rng(14)
+    x = rng.standard_normal((3, 8 * 32))
+    g = rng.normal(1, 0.1, 32)
+    y0 = oq.headwise_rmsnorm(x, g, 1e-6, 32, 0)
+    x2 = x.copy()
+    x2[:, 96:128] *= 17.0
+    y1 = oq.headwise_rmsnorm(x2, g, 1e-6, 32, 0)
+    assert np.array_equal(np.delete(y0, np.s_[96:128], axis=1), np.delete(y1, np.s_[96:128], axis=1))
+    assert not np.array_equal(y0[:, 96:128], y1[:, 96:128])
+
+
+def pin_headwise_top_level():
+    """Q and K with different head counts, each head over head_dim; bf16 bits rounded once."""
+    rng = _rng(15)
+    T, hd = 4, 32
+    xq = obf16.f64_to_bf16_bits(rng.standard_normal((T, 5 * hd)))
+    xk = obf16.f64_to_bf16_bits(rng.standard_normal((T, 2 * hd)))
+    gq = obf16.f64_to_bf16_bits(rng.normal(1, 0.1, hd))
+    gk = obf16.f64_to_bf16_bits(rng.normal(1, 0.1, hd))
+    r = oq.qknorm_headwise(xq, xk, gq, gk, "bf16", 1e-6, hd, 0)
+    e = float(np.float32(1e-6))
+    for x, g, y in ((xq, gq, r.yq), (xk, gk, r.yk)):
+        xd = obf16.bf16_bits_to_f64(x).reshape(T, -1, hd)
+        d = np.sqrt(np.mean(xd * xd, axis=2, keepdims=True) + e)
+        _close(y, (xd * obf16.bf16_bits_to_f64(g) / d).reshape(T, -1), rel=1e-15)
+    assert np.array_equal(r.yq_bits, obf16.f64_to_bf16_bits(r.yq))
+
+
 ALL_PINS = [
     pin_golden_worked_examples,
     pin_golden_bf16_rounding,
@@ -309,6 +374,11 @@ ALL_PINS = [
     pin_apply_local_slice,
     pin_top_level_calls,
     pin_nonfinite_and_zero_rows,
+    pin_headwise_one_head_is_layerwise,
+    pin_headwise_torch_rms_norm_fp64,
+    pin_headwise_constant_heads,
+    pin_headwise_heads_independent,
+    pin_headwise_top_level,
 ]
 
 assert oracle.qknorm_fused is oq.qknorm_fused

@@ -79,6 +79,37 @@ def _fused_joint(xq, xk, gamma_q, gamma_k, dtype, eps, shards):
     return oq.QKResult(y[:, :hq], y[:, hq:], dtype, pq, pk)
 
 
+def _headwise_as_layerwise(x, gamma, eps, head_dim, gamma_head_stride):
+    g = np.asarray(gamma, np.float64)
+    h = np.asarray(x).shape[1]
+    full = np.concatenate([g[i * gamma_head_stride:i * gamma_head_stride + head_dim] for i in range(h // head_dim)])
+    return oq.layerwise_rmsnorm(x, full, eps)[0]
+
+
+def _headwise_stride(forced):
+    def f(x, gamma, eps, head_dim, gamma_head_stride):
+        g = np.asarray(gamma, np.float64)
+        stride = head_dim if forced == "full" else 0
+        return _orig_headwise(x, g, eps, head_dim, stride)
+    return f
+
+
+def _headwise_shifted(x, gamma, eps, head_dim, gamma_head_stride):
+    x = np.asarray(x, np.float64)
+    y = np.empty_like(x)
+    h = x.shape[1]
+    g = np.asarray(gamma, np.float64)
+    for head in range(h // head_dim):
+        lo = max(head * head_dim - 1, 0)
+        cols = slice(lo, lo + head_dim)
+        g0 = head * gamma_head_stride
+        yh = oq.layerwise_rmsnorm(x[:, cols], g[g0:g0 + head_dim], eps)[0]
+        y[:, head * head_dim:(head + 1) * head_dim] = yh
+    return y
+
+
+_orig_headwise = oq.headwise_rmsnorm
+
 MUTANTS = {
     "eps_dropped": ("rms_denominator", lambda ss, h, eps: np.sqrt(np.asarray(ss) / float(h))),
     "eps_outside_sqrt": ("rms_denominator", lambda ss, h, eps: np.sqrt(np.asarray(ss) / float(h)) + eps),
@@ -105,6 +136,10 @@ MUTANTS = {
     "decode_bf16_shift15": ("bf16_bits_to_f64", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)),
     "q_k_gamma_swapped": ("qknorm_fused", _fused_gamma_swapped),
     "q_k_normalized_jointly": ("qknorm_fused", _fused_joint),
+    "headwise_one_factor_per_row": ("headwise_rmsnorm", _headwise_as_layerwise),
+    "headwise_gamma_always_shared": ("headwise_rmsnorm", _headwise_stride("shared")),
+    "headwise_gamma_always_per_column": ("headwise_rmsnorm", _headwise_stride("full")),
+    "headwise_heads_shifted_by_one_column": ("headwise_rmsnorm", _headwise_shifted),
 }
 
 
