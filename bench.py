@@ -72,19 +72,29 @@ class FusedStep:
             x = x0 if i == 0 else x0.clone()
             y = torch.zeros_like(x0)
             self.sets.append((x, y))
-        self.gq = to_device(inp.gamma_q, dev)
-        self.gk = to_device(inp.gamma_k, dev)
         esz = x0.element_size()
-        self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+        if w.head_dim:   # headwise: one shared [head_dim] gamma per tensor
+            self.gq = to_device(inp.gamma_q[:w.head_dim], dev)
+            self.gk = to_device(inp.gamma_k[:w.head_dim], dev)
+            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + 2 * w.head_dim * esz
+            self.name = "qknorm_headwise"
+        else:
+            self.gq = to_device(inp.gamma_q, dev)
+            self.gk = to_device(inp.gamma_k, dev)
+            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+            self.name = "qknorm_fused"
         self.footprint = self.n_sets * per_set
         self.launches = 1
-        self.name = "qknorm_fused"
 
     def __call__(self, i):
         x, y = self.sets[i % self.n_sets]
         hq, hk = self.w.hq, self.w.hk
-        self.qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.shards,
-                             y[:, :hq], y[:, hq:hq + hk])
+        if self.w.head_dim:
+            self.qk.qknorm_headwise(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.w.head_dim, 0,
+                                    y[:, :hq], y[:, hq:hq + hk])
+        else:
+            self.qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.shards,
+                                 y[:, :hq], y[:, hq:hq + hk])
 
 
 class SplitStep:
@@ -196,6 +206,9 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
             st = np.concatenate([local, peer_planes[:, :, a:b]])
             oracle.qknorm_apply_with_stats(inp.q[a:b], inp.k[a:b], inp.gamma_q, inp.gamma_k, w.dtype, w.eps, st,
                                            w.hq_full, w.hk_full)
+        elif w.head_dim:
+            oracle.qknorm_headwise(inp.q[a:b], inp.k[a:b], inp.gamma_q[:w.head_dim], inp.gamma_k[:w.head_dim],
+                                   w.dtype, w.eps, w.head_dim, 0)
         else:
             oracle.qknorm_fused(inp.q[a:b], inp.k[a:b], inp.gamma_q, inp.gamma_k, w.dtype, w.eps, w.shards[0])
         return b - a
@@ -442,7 +455,10 @@ def main():
         plan = "; ".join(qk.describe_plan(op, w.hq, w.hk, w.T, w.dtype, 1, ld=w.ld) for op in (1, 2))
     else:
         step = FusedStep(w, inp, dev, shards)
-        plan = qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq)
+        if w.head_dim:
+            plan = qk.describe_headwise_plan(w.hq, w.hk, w.T, w.head_dim, w.dtype, 0, ld=w.ld)
+        else:
+            plan = qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq)
     torch.cuda.synchronize()
     log(f"[bench] plan: {plan}; {step.n_sets} rotating buffer sets, {step.footprint / 2**20:.0f} MiB")
 

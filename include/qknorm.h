@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define QKNORM_ABI_VERSION 1
+#define QKNORM_ABI_VERSION 2
 
 /* Largest shard count and number of statistic planes accepted. */
 #define QKNORM_MAX_SHARDS 64
@@ -164,6 +164,31 @@ int qknorm_apply_with_stats(const qknorm_operand_t* q, const qknorm_operand_t* k
                             int dtype, float eps, const float* stats, int n_planes,
                             int64_t hq_full, int64_t hk_full, void* stream);
 
+/*
+ * qknorm_headwise -- headwise QK-Norm: the paper's introduction names this
+ * granularity as one independent normalization factor per attention head.
+ * Every head (head_dim contiguous columns; Q has q->h / head_dim heads and K
+ * has k->h / head_dim) is normalized with Eq. 1 on its own, H = head_dim:
+ * y_j = (x_j * gamma_j) * rsqrt(sum over the head of x^2 / head_dim + eps),
+ * with the same float32 arithmetic as the layerwise calls. There is no
+ * combination across heads, so nothing here needs an exchange between
+ * tensor-parallel ranks.
+ *
+ *   head_dim           > 0; q->h and k->h must be multiples of it
+ *   gamma_head_stride  gamma element (head, j) is gamma[head * stride + j]:
+ *                      0 shares one [head_dim] vector across heads (the usual
+ *                      per-head RMSNorm weight), head_dim reads a full [h]
+ *                      vector; any stride >= 0 is accepted
+ *   q, k, T, dtype, eps, stream as for qknorm_fused (gamma holds
+ *   (heads - 1) * stride + head_dim elements).
+ *
+ * Heads of up to 4096 bf16 / 2048 fp32 elements and up to 256 heads per
+ * token (Q and K together) are supported; larger ones return
+ * QKNORM_ERR_UNSUPPORTED.
+ */
+int qknorm_headwise(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype,
+                    float eps, int64_t head_dim, int64_t gamma_head_stride, void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* qknorm_last_error(void);
 
@@ -180,6 +205,11 @@ int qknorm_abi_version(void);
  */
 int qknorm_describe_plan(int op, const qknorm_operand_t* q, const qknorm_operand_t* k,
                          int64_t T, int dtype, int shards, char* buf, size_t len);
+
+/* As qknorm_describe_plan, for qknorm_headwise. */
+int qknorm_describe_headwise_plan(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T,
+                                  int dtype, int64_t head_dim, int64_t gamma_head_stride, char* buf,
+                                  size_t len);
 
 #ifdef __cplusplus
 }

@@ -8,10 +8,12 @@ call does, and raises if the library has not been built.
 from .binding import (  # noqa: F401
     QKNormError,
     abi_version,
+    describe_headwise_plan,
     describe_plan,
     library_path,
     load_library,
     qknorm_apply_with_stats,
     qknorm_fused,
+    qknorm_headwise,
     qknorm_partial_stats,
 )

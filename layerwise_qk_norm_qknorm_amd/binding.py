@@ -23,9 +23,9 @@ QKNORM_ERR_INVALID_ARG = 1
 QKNORM_ERR_UNSUPPORTED = 2
 QKNORM_ERR_HIP = 3
 OP_FUSED, OP_PARTIAL_STATS, OP_APPLY_WITH_STATS = 0, 1, 2
-ABI_VERSION = 1
-EXPORTS = ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats",
-           "qknorm_last_error", "qknorm_abi_version", "qknorm_describe_plan")
+ABI_VERSION = 2
+EXPORTS = ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats", "qknorm_headwise",
+           "qknorm_last_error", "qknorm_abi_version", "qknorm_describe_plan", "qknorm_describe_headwise_plan")
 
 
 class QKNormError(RuntimeError):
@@ -73,8 +73,10 @@ def load_library():
         lib.qknorm_partial_stats.argtypes = [P, P, i64, ci, ci, vp, vp]
         lib.qknorm_apply_with_stats.argtypes = [P, P, i64, ci, fl, vp, ci, i64, i64, vp]
         lib.qknorm_describe_plan.argtypes = [ci, P, P, i64, ci, ci, ctypes.c_char_p, ctypes.c_size_t]
-        for fn in ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats",
-                   "qknorm_describe_plan", "qknorm_abi_version"):
+        lib.qknorm_headwise.argtypes = [P, P, i64, ci, fl, i64, i64, vp]
+        lib.qknorm_describe_headwise_plan.argtypes = [P, P, i64, ci, i64, i64, ctypes.c_char_p, ctypes.c_size_t]
+        for fn in ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats", "qknorm_headwise",
+                   "qknorm_describe_plan", "qknorm_describe_headwise_plan", "qknorm_abi_version"):
             getattr(lib, fn).restype = ci
         lib.qknorm_last_error.restype = ctypes.c_char_p
         lib.qknorm_last_error.argtypes = []
@@ -207,6 +209,43 @@ def qknorm_apply_with_stats(q, k, gamma_q, gamma_k, eps, stats, hq_full, hk_full
                                        stats.data_ptr(), int(stats.shape[0]), int(hq_full), int(hk_full),
                                        _stream(q, stream)))
     return out_q, out_k
+
+
+def qknorm_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, out_q=None, out_k=None,
+                    stream=None):
+    """Headwise QK-Norm of q [T, hq] and k [T, hk]: every head of ``head_dim``
+    columns normalized on its own. gamma element (head, j) is
+    gamma[head * gamma_head_stride + j] (0: one [head_dim] vector shared by all
+    heads). Writes ``out_q``/``out_k`` (default: in place) and returns them."""
+    lib = load_library()
+    T = _tokens(q, k)
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, None, "q")
+    ok = _operand(k, out_k, None, "k")
+    for g, o, name in ((gamma_q, oq, "q"), (gamma_k, ok, "k")):
+        need = (o.h // head_dim - 1) * gamma_head_stride + head_dim if head_dim > 0 else 0
+        if g.dim() != 1 or g.shape[0] < need or (g.shape[0] > 1 and g.stride(0) != 1) or g.dtype != q.dtype:
+            raise ValueError(f"gamma for {name} must be contiguous, dtype {q.dtype}, >= {need} elements")
+        o.gamma = g.data_ptr()
+    _check(lib.qknorm_headwise(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), int(head_dim),
+                               int(gamma_head_stride), _stream(q, stream)))
+    return out_q, out_k
+
+
+def describe_headwise_plan(hq, hk, T, head_dim, dtype="bf16", gamma_head_stride=0, ld=None):
+    """The launch qknorm_headwise would make, for shapes alone (no GPU needed)."""
+    lib = load_library()
+    code = QKNORM_BF16 if dtype == "bf16" else QKNORM_F32
+    esz = 2 if dtype == "bf16" else 4
+    ld = ld if ld is not None else hq + hk
+    xq, xk = (1 << 32), (1 << 32) + hq * esz if ld >= hq + hk else (1 << 40)
+    oq = Operand(xq, ld, xq + (1 << 44), ld, 1 << 46, hq)
+    ok = Operand(xk, ld, xk + (1 << 44), ld, (1 << 46) + (1 << 30), hk)
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.qknorm_describe_headwise_plan(ctypes.byref(oq), ctypes.byref(ok), T, code, head_dim,
+                                             gamma_head_stride, buf, 512))
+    return buf.value.decode()
 
 
 def describe_plan(op, hq, hk, T, dtype="bf16", shards=1, ld=None, aligned=True):

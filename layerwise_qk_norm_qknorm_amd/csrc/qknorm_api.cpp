@@ -231,6 +231,102 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   return QKNORM_OK;
 }
 
+struct HeadChecked {
+  qkn::Plan plan;
+  qkn::HeadArgs args;
+};
+
+// Validation and planning for qknorm_headwise (no HIP calls).
+int check_and_plan_heads(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype, float eps,
+                         int64_t head_dim, int64_t gstride, HeadChecked* out, bool* noop) {
+  const char* fn = "qknorm_headwise";
+  *noop = false;
+  if (!q || !k) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k operand descriptors are required", fn);
+  const size_t esz = elem_size(dtype);
+  if (!esz) return fail(QKNORM_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (T < 0) return fail(QKNORM_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (!(std::isfinite(eps) && eps >= 0.0f)) return fail(QKNORM_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (head_dim <= 0 || head_dim > ((int64_t)1 << 20))
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: head_dim = %lld", fn, (long long)head_dim);
+  if (gstride < 0 || gstride > ((int64_t)1 << 30))
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: gamma_head_stride = %lld", fn, (long long)gstride);
+  const qknorm_operand_t* ops[2] = {q, k};
+  const char* nm[2] = {"q", "k"};
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    if (o->h <= 0 || o->h % head_dim)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->h = %lld is not a positive multiple of head_dim %lld", fn, nm[c],
+                  (long long)o->h, (long long)head_dim);
+    if (o->ld_x < o->h || o->ld_y < o->h)
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s row strides must be >= h", fn, nm[c]);
+    if (o->h > (int64_t)1 << 30) return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s->h is too wide", fn, nm[c]);
+  }
+  if (T == 0) {
+    *noop = true;
+    return ok();
+  }
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    if (!o->x || !o->y || !o->gamma) return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->x, y and gamma are required", fn, nm[c]);
+    if (!fits(T, o->ld_x, o->h, esz) || !fits(T, o->ld_y, o->h, esz))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s rows exceed the address range", fn, nm[c]);
+  }
+  const int64_t e = (int64_t)esz;
+  Region xr[2], yr[2], gr[2];
+  for (int c = 0; c < 2; ++c) {
+    const int64_t heads = ops[c]->h / head_dim;
+    xr[c] = Region{(uintptr_t)ops[c]->x, ops[c]->ld_x, ops[c]->h, T, e};
+    yr[c] = Region{(uintptr_t)ops[c]->y, ops[c]->ld_y, ops[c]->h, T, e};
+    const int64_t gext = (heads - 1) * gstride + head_dim;  // gamma elements read
+    gr[c] = Region{(uintptr_t)ops[c]->gamma, gext, gext, 1, e};
+  }
+  if (may_overlap(yr[0], yr[1])) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k outputs overlap", fn);
+  for (int c = 0; c < 2; ++c) {
+    if (may_overlap(yr[c], xr[1 - c]))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s output overlaps the %s input", fn, nm[c], nm[1 - c]);
+    if (may_overlap(yr[c], xr[c]) && !same_region(yr[c], xr[c]))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s output partially overlaps its input", fn, nm[c]);
+    for (int g = 0; g < 2; ++g)
+      if (may_overlap(yr[c], gr[g]))
+        return fail(QKNORM_ERR_INVALID_ARG, "%s: %s output overlaps gamma of %s", fn, nm[c], nm[g]);
+  }
+  const int vw = (int)(16 / esz);
+  bool aligned = head_dim % vw == 0 && gstride % vw == 0;
+  for (int c = 0; c < 2; ++c) {
+    const qknorm_operand_t* o = ops[c];
+    aligned = aligned && (uintptr_t)o->x % 16 == 0 && (uintptr_t)o->y % 16 == 0 && (uintptr_t)o->gamma % 16 == 0 &&
+              o->ld_x % vw == 0 && o->ld_y % vw == 0;
+  }
+  std::string why;
+  if (!qkn::make_head_plan(dtype == QKNORM_BF16, aligned, head_dim, q->h / head_dim, k->h / head_dim, T, &out->plan,
+                           &why))
+    return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  qkn::HeadArgs& a = out->args;
+  std::memset(&a, 0, sizeof a);
+  a.xq = q->x;
+  a.yq = q->y;
+  a.gq = q->gamma;
+  a.ldxq = q->ld_x;
+  a.ldyq = q->ld_y;
+  a.xk = k->x;
+  a.yk = k->y;
+  a.gk = k->gamma;
+  a.ldxk = k->ld_x;
+  a.ldyk = k->ld_y;
+  a.T = T;
+  a.gstride = gstride;
+  a.head_dim = (int)head_dim;
+  a.heads_q = out->plan.heads_q;
+  a.heads_k = out->plan.heads_k;
+  a.nc = out->plan.ncq;
+  a.lanes = out->plan.lanes;
+  a.tok_threads = out->plan.tok_threads;
+  a.tokens_per_block = out->plan.tokens_per_block;
+  a.div = (float)head_dim;
+  a.eps = eps;
+  return QKNORM_OK;
+}
+
 int run(int mode, const Checked& c, void* stream) {
   std::string err;
   const int rc = qkn::launch(c.plan, c.args, stream, &err);
@@ -330,7 +426,117 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
   return true;
 }
 
+// Headwise launch geometry: the same rule as the layerwise planner (about 3
+// chunks per lane, few idle slots; few tokens: fewer chunks per lane), with
+// a group of L lanes per head and blocks of about 512 threads.
+bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
+                    Plan* p, std::string* why) {
+  Plan r;
+  r.mode = MODE_HEADWISE;
+  r.bf16 = bf16 ? 1 : 0;
+  r.aligned = aligned ? 1 : 0;
+  r.vw = bf16 ? 8 : 4;
+  const int64_t nc = (head_dim + r.vw - 1) / r.vw;
+  const int64_t heads = heads_q + heads_k;
+  if (nc > 64 * 8) {
+    *why = "heads of " + std::to_string(head_dim) + " elements exceed the " + std::to_string(64 * 8 * r.vw) +
+           " a lane group holds";
+    return false;
+  }
+  if (heads * kMinLanesPerShard > kMaxThreads) {
+    *why = std::to_string(heads) + " heads per token exceed the " + std::to_string(kMaxThreads / kMinLanesPerShard) +
+           " a block holds";
+    return false;
+  }
+  const bool few_tokens = T < 1024;
+  r.heads_q = (int)heads_q;
+  r.heads_k = (int)heads_k;
+  r.head_dim = (int)head_dim;
+  r.ncq = (int)nc;
+  r.shards = (int)heads;
+
+  // A head of a power-of-two number of chunks (<= 64) fits an aligned lane
+  // group, so the token's chunks can be laid out as in the layerwise kernel
+  // (consecutive chunks on consecutive lanes), a slot per lane group per head.
+  const int64_t total = heads * nc;
+  if ((nc & (nc - 1)) == 0 && nc <= 64 && total <= (int64_t)kMaxThreads * 8) {
+    int best_g = 0, best_v = 0;
+    double best_score = 1e30;
+    for (int g = 64; g <= kMaxThreads; g += 64) {
+      const int v = slots_for((int)((total + g - 1) / g));
+      if (!v || g > max_threads_for_slots(v)) continue;
+      const double wfrac = (double)((int64_t)g * v - total) / (double)(g * v);
+      const double score = few_tokens
+          ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
+          : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (g / 64);
+      if (score < best_score) {
+        best_score = score;
+        best_g = g;
+        best_v = v;
+      }
+    }
+    if (best_g) {
+      r.heads_packed = 1;
+      r.lanes = (int)nc;
+      r.group = (int)nc;
+      r.slots = best_v;
+      r.tok_threads = best_g;
+      r.tokens_per_block = (best_g == 64 && !few_tokens) ? 4 : 1;
+      if (r.tokens_per_block * best_g > max_threads_for_slots(best_v)) r.tokens_per_block = 1;
+      r.threads = r.tokens_per_block * best_g;
+      r.waves = r.threads / 64;
+      *p = r;
+      return true;
+    }
+  }
+
+  int best_l = 0, best_v = 0;
+  double best_score = 1e30;
+  for (int l = kMinLanesPerShard; l <= 64; l *= 2) {
+    const int v = slots_for(ceil_div((int)nc, l));
+    if (!v) continue;
+    const int64_t g = heads * l;
+    const int64_t threads = (g + 63) / 64 * 64;
+    if (threads > max_threads_for_slots(v)) continue;
+    const double wfrac = (double)((int64_t)l * v - nc) / (double)(l * v);
+    const double score = few_tokens
+        ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
+        : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (double)threads / 64;
+    if (score < best_score) {
+      best_score = score;
+      best_l = l;
+      best_v = v;
+    }
+  }
+  if (!best_l) {
+    *why = "no lane layout holds " + std::to_string(heads) + " heads of " + std::to_string(nc) + " chunks";
+    return false;
+  }
+  r.lanes = best_l;
+  r.group = best_l;
+  r.slots = best_v;
+  r.tok_threads = (int)heads * best_l;
+  int tpb = few_tokens ? 1 : (int)(512 / r.tok_threads);
+  if (tpb < 1) tpb = 1;
+  while (tpb > 1 && (tpb * r.tok_threads + 63) / 64 * 64 > max_threads_for_slots(best_v)) --tpb;
+  r.tokens_per_block = tpb;
+  r.threads = (tpb * r.tok_threads + 63) / 64 * 64;
+  r.waves = r.threads / 64;
+  *p = r;
+  return true;
+}
+
 std::string describe(const Plan& p) {
+  if (p.mode == MODE_HEADWISE) {
+    char buf[320];
+    snprintf(buf, sizeof buf,
+             "headwise %s path=%s layout=%s heads=(%d,%d) head_dim=%d chunks/head=%d lanes/head=%d "
+             "threads/token=%d tokens/block=%d threads/block=%d slots=%d",
+             p.bf16 ? "bf16" : "f32", p.aligned ? "16B" : "elementwise", p.heads_packed ? "token-wide" : "per-head",
+             p.heads_q, p.heads_k, p.head_dim, p.ncq, p.heads_packed ? p.ncq : p.lanes, p.tok_threads,
+             p.tokens_per_block, p.threads, p.slots);
+    return buf;
+  }
   char buf[320];
   snprintf(buf, sizeof buf,
            "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads/token=%d "
@@ -376,6 +582,29 @@ int qknorm_apply_with_stats(const qknorm_operand_t* q, const qknorm_operand_t* k
 }
 
 const char* qknorm_last_error(void) { return g_last_error.c_str(); }
+
+int qknorm_headwise(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype, float eps,
+                    int64_t head_dim, int64_t gamma_head_stride, void* stream) {
+  HeadChecked c;
+  bool noop;
+  const int rc = check_and_plan_heads(q, k, T, dtype, eps, head_dim, gamma_head_stride, &c, &noop);
+  if (rc || noop) return rc;
+  std::string err;
+  if (qkn::launch_heads(c.plan, c.args, stream, &err)) return fail(QKNORM_ERR_HIP, "qknorm_headwise: %s", err.c_str());
+  return ok();
+}
+
+int qknorm_describe_headwise_plan(const qknorm_operand_t* q, const qknorm_operand_t* k, int64_t T, int dtype,
+                                  int64_t head_dim, int64_t gamma_head_stride, char* buf, size_t len) {
+  if (!buf || !len) return fail(QKNORM_ERR_INVALID_ARG, "qknorm_describe_headwise_plan: no output buffer");
+  HeadChecked c;
+  bool noop;
+  const int rc = check_and_plan_heads(q, k, T, dtype, 1e-6f, head_dim, gamma_head_stride, &c, &noop);
+  if (rc) return rc;
+  const std::string s = noop ? std::string("no-op (T = 0)") : qkn::describe(c.plan);
+  snprintf(buf, len, "%s", s.c_str());
+  return ok();
+}
 
 int qknorm_abi_version(void) { return QKNORM_ABI_VERSION; }
 

@@ -8,7 +8,7 @@
 
 namespace qkn {
 
-enum Mode : int { MODE_FUSED = 0, MODE_STATS = 1, MODE_APPLY = 2 };
+enum Mode : int { MODE_FUSED = 0, MODE_STATS = 1, MODE_APPLY = 2, MODE_HEADWISE = 3 };
 
 // Chunk-slot counts per lane that have a compiled kernel.
 constexpr int kSlotSizes[] = {1, 2, 3, 4, 6, 8, 12, 16};
@@ -49,6 +49,11 @@ struct Plan {
   int slots = 0;      // chunk slots per lane (one of kSlotSizes)
   int waves = 0;      // waves per token: G / 64
   int lds_bytes = 0;  // dynamic LDS for the cross-wave reduction (0 if one wave per token)
+  // headwise only: heads of Q and of K, head width, gamma stride between heads
+  int heads_q = 0;
+  int heads_k = 0;
+  int head_dim = 0;
+  int heads_packed = 0;  // 1: token-wide chunk layout, one nc-lane group per head per slot
 };
 
 // Kernel arguments (passed by value).
@@ -72,6 +77,37 @@ struct RowArgs {
   const float* stats; // MODE_APPLY: [P][2][T]
   int n_planes;
 };
+
+// Headwise kernel arguments: every head of head_dim columns is normalized on
+// its own; a token's heads (Q heads, then K heads) each take an aligned group
+// of `lanes` lanes.
+struct HeadArgs {
+  const void* xq;
+  void* yq;
+  const void* gq;
+  int64_t ldxq, ldyq;
+  const void* xk;
+  void* yk;
+  const void* gk;
+  int64_t ldxk, ldyk;
+  int64_t T;
+  int64_t gstride;    // gamma elements between consecutive heads (0: shared)
+  int head_dim;
+  int heads_q, heads_k;
+  int nc;             // chunks per head
+  int lanes;          // per-head layout: lanes per head (power of two, 4..64);
+                      // token-wide layout: nc (the lane group of one head)
+  int tok_threads;    // threads per token
+  int tokens_per_block;
+  float div;          // head_dim, the H of Eq. 1
+  float eps;
+};
+
+// Plans a headwise launch; false (with a reason) if no kernel holds a head.
+bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
+                    Plan* plan, std::string* why);
+
+int launch_heads(const Plan& plan, const HeadArgs& args, void* stream, std::string* err);
 
 // Fills `plan` for the given shapes; returns false (with a reason) if no
 // compiled kernel can hold the row.

@@ -168,7 +168,7 @@ __device__ __forceinline__ void keep_packed(Chunk& c) {
   asm volatile("" : "+v"(c.w[0]), "+v"(c.w[1]), "+v"(c.w[2]), "+v"(c.w[3]));
 }
 
-// Sum over aligned groups of `group` lanes (a power of two, 4..64); every
+// Sum over aligned groups of `group` lanes (a power of two, 1..64); every
 // lane of a group ends with the same value. Inside a 16-lane row the steps
 // are DPP moves fused into the adds (quad permutes, then the half-row and
 // row mirrors, which pair lanes of the two halves once each half is
@@ -181,7 +181,7 @@ __device__ __forceinline__ float dpp_move(float v) {
 }
 
 __device__ __forceinline__ float group_sum(float v, int group) {
-  v += dpp_move<0xB1>(v);                   // lanes i ^ 1   (quad_perm 1,0,3,2)
+  if (group > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
   if (group > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
   if (group > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
   if (group > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
@@ -356,7 +356,181 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
   }
 }
 
+// Headwise QK-Norm (the introduction's per-head granularity): Eq. 1 for every
+// head of head_dim columns, H = head_dim, with no combination across heads.
+// Head g of a token (Q heads first, then K heads) is owned by an aligned group
+// of L lanes; lane m takes the head's chunks m, m+L, ... The group sum leaves
+// the head's sum of squares in all L lanes, so no LDS and no barrier are
+// needed. Blocks are rounded up to whole waves; lanes past the last token
+// slot only read valid addresses and write nothing.
+template <class IO, int V, bool ALIGNED>
+__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const HeadArgs a) {
+  constexpr int VW = IO::kVW;
+  const int tid = threadIdx.x;
+  const int G = a.tok_threads;
+  const int L = a.lanes;
+  const int j = tid / G;                       // token slot within the block
+  const int r = tid - j * G;
+  const bool live = j < a.tokens_per_block;    // false for the round-up lanes
+  const int seg = r / L;                       // head within the token
+  const int m = r - seg * L;
+  const bool isq = seg < a.heads_q;
+  const int head = isq ? seg : seg - a.heads_q;
+
+  int col[V], gcol[V], cnt[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int u = i * L + m;
+    if (live && u < a.nc) {
+      const int c = u * VW;
+      col[i] = head * a.head_dim + c;
+      gcol[i] = c;
+      cnt[i] = min(VW, a.head_dim - c);
+    } else {  // idle slot: reads (and ignores) the first chunk of the row and of the head's gamma
+      col[i] = 0;
+      gcol[i] = 0;
+      cnt[i] = 0;
+    }
+  }
+  // this head's gamma (head * stride elements in; the first head's for stride 0)
+  const char* gbase = static_cast<const char*>(isq ? a.gq : a.gk) + (int64_t)head * a.gstride * IO::kBytes;
+  const char* xbase = static_cast<const char*>(isq ? a.xq : a.xk);
+  char* ybase = static_cast<char*>(isq ? a.yq : a.yk);
+  const int64_t ldx = isq ? a.ldxq : a.ldxk;
+  const int64_t ldy = isq ? a.ldyq : a.ldyk;
+
+  Chunk g[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) g[i] = load_chunk<IO, ALIGNED>(gbase, gcol[i], max(cnt[i], 1));
+
+  const int tpb = a.tokens_per_block;
+  const int64_t step = (int64_t)gridDim.x * tpb;
+  for (int64_t tb = (int64_t)blockIdx.x * tpb; tb < a.T; tb += step) {
+    const int64_t t = tb + j;
+    const bool active = live && t < a.T;
+    const int64_t tr = t < a.T ? t : a.T - 1;
+    const char* x_row = xbase + tr * ldx * IO::kBytes;
+
+    Chunk xv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(x_row, col[i], max(cnt[i], 1));
+    if (IO::kBytes == 2) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) keep_packed(g[i]);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
+    acc = group_sum(acc, L);
+
+    if (active) {
+      if (IO::kBytes == 2) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) keep_packed(xv[i]);
+      }
+      const float rr = rms_factor(acc, a.div, a.eps);
+      char* y_row = ybase + t * ldy * IO::kBytes;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        if (cnt[i] > 0) {
+          float y[VW];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
+          Chunk out;
+          pack<IO>(out, y);
+          store_chunk<IO, ALIGNED>(y_row, col[i], cnt[i], out);
+        }
+      }
+    }
+  }
+}
+
+// Headwise QK-Norm when a head is a power-of-two number of chunks (up to 64,
+// e.g. 128 bf16 = 16 chunks): the token's chunks (Q heads, then K heads) are
+// laid over G lanes exactly as in the layerwise kernel, lane m of slot i
+// taking chunk i*G + m, so every load instruction reads consecutive 16-byte
+// chunks. Because G is a multiple of the head's chunk count nc, the nc
+// consecutive lanes of a slot hold exactly one head: each slot is reduced
+// over its aligned nc-lane group and scaled by that head's factor.
+template <class IO, int V, bool ALIGNED>
+__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(const HeadArgs a) {
+  constexpr int VW = IO::kVW;
+  const int tid = threadIdx.x;
+  const int G = a.tok_threads;                 // lanes per token, a multiple of 64 and of nc
+  const int nc = a.lanes;                      // chunks per head (power of two, <= 64)
+  const int j = tid / G;                       // token slot within the block
+  const int m = tid - j * G;
+  const int total = (a.heads_q + a.heads_k) * nc;
+
+  bool isq[V];
+  int col[V], cnt[V];
+  const char* gp[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int u = i * G + m;
+    if (u < total) {
+      const int head = u / nc;
+      const int c = (u - head * nc) * VW;
+      isq[i] = head < a.heads_q;
+      const int hh = isq[i] ? head : head - a.heads_q;
+      col[i] = hh * a.head_dim + c;
+      cnt[i] = min(VW, a.head_dim - c);
+      gp[i] = static_cast<const char*>(isq[i] ? a.gq : a.gk) + ((int64_t)hh * a.gstride + c) * IO::kBytes;
+    } else {  // idle slot: reads (and ignores) the first chunk of the Q row and of gamma
+      isq[i] = true;
+      col[i] = 0;
+      cnt[i] = 0;
+      gp[i] = static_cast<const char*>(a.gq);
+    }
+  }
+  Chunk g[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) g[i] = load_chunk<IO, ALIGNED>(gp[i], 0, max(cnt[i], 1));
+
+  const int tpb = a.tokens_per_block;
+  const int64_t step = (int64_t)gridDim.x * tpb;
+  for (int64_t tb = (int64_t)blockIdx.x * tpb; tb < a.T; tb += step) {
+    const int64_t t = tb + j;
+    const bool active = t < a.T;
+    const int64_t tr = active ? t : a.T - 1;
+    const char* xq_row = static_cast<const char*>(a.xq) + tr * a.ldxq * IO::kBytes;
+    const char* xk_row = static_cast<const char*>(a.xk) + tr * a.ldxk * IO::kBytes;
+    Chunk xv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
+    if (IO::kBytes == 2) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) keep_packed(g[i]);
+    }
+    float ss[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
+
+    if (active) {
+      if (IO::kBytes == 2) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) keep_packed(xv[i]);
+      }
+      char* yq_row = static_cast<char*>(a.yq) + t * a.ldyq * IO::kBytes;
+      char* yk_row = static_cast<char*>(a.yk) + t * a.ldyk * IO::kBytes;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        if (cnt[i] > 0) {
+          const float rr = rms_factor(ss[i], a.div, a.eps);
+          float y[VW];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
+          Chunk out;
+          pack<IO>(out, y);
+          store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+        }
+      }
+    }
+  }
+}
+
 using KernelFn = void (*)(const RowArgs);
+using HeadKernelFn = void (*)(const HeadArgs);
 
 constexpr int64_t kMaxGrid = (int64_t)1 << 30;
 
@@ -390,6 +564,32 @@ KernelFn pick_mode(int mode, bool aligned, int v) {
   return nullptr;
 }
 
+template <class IO, bool ALIGNED, bool PACKED>
+HeadKernelFn pick_head_slots(int v) {
+#define QKN_HEAD_KERNEL(V) (PACKED ? qknorm_heads_packed<IO, V, ALIGNED> : qknorm_heads<IO, V, ALIGNED>)
+  switch (v) {
+    case 1: return QKN_HEAD_KERNEL(1);
+    case 2: return QKN_HEAD_KERNEL(2);
+    case 3: return QKN_HEAD_KERNEL(3);
+    case 4: return QKN_HEAD_KERNEL(4);
+    case 6: return QKN_HEAD_KERNEL(6);
+    case 8: return QKN_HEAD_KERNEL(8);
+    case 12: return QKN_HEAD_KERNEL(12);
+    case 16: return QKN_HEAD_KERNEL(16);
+  }
+#undef QKN_HEAD_KERNEL
+  return nullptr;
+}
+
+template <class IO>
+HeadKernelFn pick_head_io(const Plan& p) {
+  if (p.heads_packed)
+    return p.aligned ? pick_head_slots<IO, true, true>(p.slots) : pick_head_slots<IO, false, true>(p.slots);
+  return p.aligned ? pick_head_slots<IO, true, false>(p.slots) : pick_head_slots<IO, false, false>(p.slots);
+}
+
+HeadKernelFn pick_head_kernel(const Plan& p) { return p.bf16 ? pick_head_io<BF16>(p) : pick_head_io<F32>(p); }
+
 KernelFn pick_kernel(const Plan& p) {
   return p.bf16 ? pick_mode<BF16>(p.mode, p.aligned, p.slots) : pick_mode<F32>(p.mode, p.aligned, p.slots);
 }
@@ -408,6 +608,27 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), (size_t)p.lds_bytes,
                      static_cast<hipStream_t>(stream), args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("kernel launch: ") + hipGetErrorString(e);
+    return (int)e;
+  }
+  return 0;
+}
+
+}  // namespace qkn
+
+namespace qkn {
+
+int launch_heads(const Plan& p, const HeadArgs& args, void* stream, std::string* err) {
+  HeadKernelFn fn = pick_head_kernel(p);
+  if (!fn) {
+    *err = "no kernel compiled for " + describe(p);
+    return (int)hipErrorInvalidValue;
+  }
+  const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
+  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), 0, static_cast<hipStream_t>(stream), args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = std::string("kernel launch: ") + hipGetErrorString(e);

@@ -52,6 +52,7 @@ class Workload:
     peers: int = 0             # number of peer slices drawn (rank-slice workload)
     outlier_p: float = 0.001
     outlier_mult: float = 50.0
+    head_dim: int = 0          # > 0: headwise QK-Norm over heads of this width
 
     @property
     def ld(self):
@@ -74,7 +75,13 @@ GQA_PREFILL = Workload("gqa_prefill", "GQA prefill: T=8192, bf16 packed [8192, 7
 RANK_SLICE = Workload("rank_slice", "Rank slice: T=16384, local 1280/256 of 5120/1024, bf16 packed [16384, 1792]",
               5, 16384, 1280, 256, 256, "bf16", True, (1,), hq_full=5120, hk_full=1024, peers=3)
 
-WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE)}
+# The GQA prefill inputs normalized headwise: 40 Q heads and 8 K heads of 128,
+# one shared [128] gamma per tensor (the first 128 entries of the drawn gamma).
+GQA_PREFILL_HEADWISE = replace(GQA_PREFILL, key="gqa_prefill_headwise",
+                               title="GQA prefill, headwise: T=8192, 40+8 heads of 128, bf16 packed [8192, 7168]",
+                               head_dim=128)
+
+WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE, GQA_PREFILL_HEADWISE)}
 
 
 def _rng(cfg_id, stream):

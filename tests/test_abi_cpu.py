@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert qk.abi_version() == 1
+    assert qk.abi_version() == 2
 
 
 # stand-in addresses: packed rows, outputs elsewhere
@@ -196,3 +196,45 @@ def test_binding_refuses_cpu_tensors():
     g = torch.ones(32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qk.qknorm_fused(x[:, :32], x[:, 32:], g, g, 1e-6, 1)
+
+
+def headwise(q, k, T=16, dtype=BF16, eps=1e-6, head_dim=64, stride=0):
+    lib = qk.load_library()
+    return lib.qknorm_headwise(ctypes.byref(q), ctypes.byref(k), T, dtype, eps, head_dim, stride, None)
+
+
+def test_headwise_rejects():
+    q, k = ops(hq=256, hk=128)
+    assert headwise(q, k, T=0) == 0
+    assert headwise(q, k, head_dim=0) == INVALID
+    assert headwise(q, k, head_dim=96) == INVALID          # 256 % 96 != 0
+    assert headwise(q, k, stride=-1) == INVALID
+    assert headwise(q, k, eps=float("nan")) == INVALID
+    assert headwise(q, k, T=-3) == INVALID
+    assert headwise(q, k, dtype=5) == INVALID
+    q2, k2 = ops(hq=256, hk=128)
+    k2.y = q2.y + 64 * 2                                    # K output over Q output
+    assert headwise(q2, k2) == INVALID
+    q3, k3 = ops(hq=256, hk=128)
+    q3.gamma = q3.y                                         # gamma inside an output
+    assert headwise(q3, k3) == INVALID
+    assert last_error().startswith("qknorm_headwise:")
+
+
+def test_headwise_plans():
+    # heads of 16 chunks: token-wide layout, 768 chunks over 256 lanes, a 16-lane group per head
+    d = qk.describe_headwise_plan(5120, 1024, 8192, 128, ld=7168)
+    assert "heads=(40,8)" in d and "layout=token-wide" in d and "lanes/head=16" in d and "slots=3" in d
+    # heads of 18 fp32 chunks (not a power of two): one lane group per head
+    d = qk.describe_headwise_plan(576, 144, 33, 72, "f32")
+    assert "layout=per-head" in d
+    d = qk.describe_headwise_plan(4096, 4096, 1, 128, ld=12288)
+    assert "slots=1" in d                                   # one token: one chunk per lane
+    d = qk.describe_headwise_plan(36 * 4, 36 * 2, 100, 36)
+    assert "elementwise" in d                               # 36 bf16 is not whole 16-byte chunks
+    with pytest.raises(qk.QKNormError) as e:
+        qk.describe_headwise_plan(8192, 8192, 4, 8192)      # a head wider than a lane group holds
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(qk.QKNormError) as e:
+        qk.describe_headwise_plan(257 * 8, 8, 4, 8)         # more heads than a block holds
+    assert e.value.status == UNSUPPORTED
