@@ -25,8 +25,11 @@ page of the paper.
 * Fig. 2(b): the precision study compares against an FP64 RMSNorm over the
   full vector, which is what this oracle is (every step in float64).
 
-All arithmetic is float64. bf16 inputs are decoded exactly; bf16 outputs are
-rounded once, from the float64 result, to the nearest bf16 (ties to even).
+All arithmetic is float64. bf16 and FP8 E4M3 inputs are decoded exactly;
+bf16 and FP8 outputs are rounded once, from the float64 result, to the nearest
+representable value (ties to even; FP8 saturates to +-448). With FP8 rows,
+gamma is bf16 (Fig. 2(b) evaluates FP8-E4M3 activations with FP32
+accumulation; the weight format is not stated, bf16 is the reading taken).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 invariants, a library special case (``torch.nn.functional.rms_norm`` in fp64),
@@ -34,6 +37,7 @@ exact rational brute force and the hand-worked examples in ``tests/golden/``.
 """
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits  # noqa: F401
+from .fp8 import f64_to_fp8_bits, fp8_bits_to_f64  # noqa: F401
 from .qknorm import (  # noqa: F401
     decode_input,
     shard_sum_of_squares,

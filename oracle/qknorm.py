@@ -24,6 +24,7 @@ is a plain ``numpy.sum`` over float64 values.
 import numpy as np
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+from .fp8 import f64_to_fp8_bits, fp8_bits_to_f64
 
 
 # --------------------------------------------------------------------------
@@ -34,12 +35,22 @@ def decode_input(a, dtype):
 
     ``dtype == "bf16"``: ``a`` holds bf16 bit patterns (uint16).
     ``dtype == "f32"``:  ``a`` holds float32 values.
+    ``dtype == "fp8"``:  ``a`` holds FP8 E4M3 (E4M3FN) bit patterns (uint8).
     """
     if dtype == "bf16":
         return bf16_bits_to_f64(a)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_bits_to_f64(a)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def decode_gamma(a, dtype):
+    """Exact float64 value of gamma: bf16 bit patterns for bf16 and FP8 rows
+    (FP8 E4M3 is the activation format; the scale stays in bf16), float32
+    values for float32 rows."""
+    return decode_input(a, "bf16" if dtype == "fp8" else dtype)
 
 
 def eps_as_passed(eps):
@@ -145,7 +156,7 @@ class QKResult:
     """Oracle outputs for one call.
 
     ``yq``/``yk``: float64 results. ``yq_bits``/``yk_bits``: the bf16 result
-    rounded once from float64 (bf16 I/O only, else None). ``pq``/``pk``:
+    rounded once from float64 (bf16 or FP8 I/O; None for float32). ``pq``/``pk``:
     float64 shard partials [S, T] (fused only, else None).
     """
 
@@ -157,6 +168,9 @@ class QKResult:
         if dtype == "bf16":
             self.yq_bits = f64_to_bf16_bits(yq)
             self.yk_bits = f64_to_bf16_bits(yk)
+        elif dtype == "fp8":
+            self.yq_bits = f64_to_fp8_bits(yq)
+            self.yk_bits = f64_to_fp8_bits(yk)
         else:
             self.yq_bits = None
             self.yk_bits = None
@@ -169,8 +183,8 @@ def qknorm_fused(xq, xk, gamma_q, gamma_k, dtype, eps, shards):
     shards; H is the whole local width (hq for Q, hk for K).
     """
     e = eps_as_passed(eps)
-    yq, pq = layerwise_rmsnorm(decode_input(xq, dtype), decode_input(gamma_q, dtype), e, shards)
-    yk, pk = layerwise_rmsnorm(decode_input(xk, dtype), decode_input(gamma_k, dtype), e, shards)
+    yq, pq = layerwise_rmsnorm(decode_input(xq, dtype), decode_gamma(gamma_q, dtype), e, shards)
+    yk, pk = layerwise_rmsnorm(decode_input(xk, dtype), decode_gamma(gamma_k, dtype), e, shards)
     return QKResult(yq, yk, dtype, pq, pk)
 
 
@@ -190,14 +204,14 @@ def qknorm_apply_with_stats(xq, xk, gamma_q, gamma_k, dtype, eps, stats, hq_full
     """
     e = eps_as_passed(eps)
     st = np.asarray(stats, dtype=np.float32).astype(np.float64)
-    yq = apply_with_stats(decode_input(xq, dtype), decode_input(gamma_q, dtype), st[:, 0, :], hq_full, e)
-    yk = apply_with_stats(decode_input(xk, dtype), decode_input(gamma_k, dtype), st[:, 1, :], hk_full, e)
+    yq = apply_with_stats(decode_input(xq, dtype), decode_gamma(gamma_q, dtype), st[:, 0, :], hq_full, e)
+    yk = apply_with_stats(decode_input(xk, dtype), decode_gamma(gamma_k, dtype), st[:, 1, :], hk_full, e)
     return QKResult(yq, yk, dtype)
 
 
 def qknorm_headwise(xq, xk, gamma_q, gamma_k, dtype, eps, head_dim, gamma_head_stride):
     """Headwise QK-Norm of Q rows and, separately, K rows (heads of head_dim)."""
     e = eps_as_passed(eps)
-    yq = headwise_rmsnorm(decode_input(xq, dtype), decode_input(gamma_q, dtype), e, head_dim, gamma_head_stride)
-    yk = headwise_rmsnorm(decode_input(xk, dtype), decode_input(gamma_k, dtype), e, head_dim, gamma_head_stride)
+    yq = headwise_rmsnorm(decode_input(xq, dtype), decode_gamma(gamma_q, dtype), e, head_dim, gamma_head_stride)
+    yk = headwise_rmsnorm(decode_input(xk, dtype), decode_gamma(gamma_k, dtype), e, head_dim, gamma_head_stride)
     return QKResult(yq, yk, dtype)

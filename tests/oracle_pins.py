@@ -358,6 +358,29 @@ def pin_headwise_top_level():
     assert np.array_equal(r.yq_bits, obf16.f64_to_bf16_bits(r.yq))
 
 
+def pin_fp8_top_level():
+    """FP8 E4M3 rows with bf16 gamma: the result is Eq. 1 on the exact decoded
+    values, rounded once to E4M3 with saturation; sums of squares are exact
+    on small integers."""
+    from oracle import fp8 as ofp8
+    rng = _rng(16)
+    T, hq, hk = 5, 64, 32
+    xq = ofp8.f64_to_fp8_bits(rng.standard_normal((T, hq)) * 3)
+    xk = ofp8.f64_to_fp8_bits(rng.integers(-8, 9, (T, hk)).astype(np.float64))
+    gq = obf16.f64_to_bf16_bits(rng.normal(1, 0.1, hq))
+    gk = obf16.f64_to_bf16_bits(np.full(hk, 300.0))          # drives some outputs past 448
+    r = oq.qknorm_fused(xq, xk, gq, gk, "fp8", 1e-6, 2)
+    e = float(np.float32(1e-6))
+    xqd = ofp8.fp8_bits_to_f64(xq)
+    dq = np.sqrt(np.mean(xqd * xqd, axis=1) + e)
+    _close(r.yq, xqd * obf16.bf16_bits_to_f64(gq) / dq[:, None], rel=1e-15)
+    assert np.array_equal(r.yq_bits, ofp8.f64_to_fp8_bits(r.yq))
+    xkd = ofp8.fp8_bits_to_f64(xk)
+    assert np.array_equal(r.pk.sum(axis=0), (xkd * xkd).sum(axis=1))  # integers: exact
+    big = np.abs(r.yk) > 464
+    assert big.any() and np.all((r.yk_bits[big] & 0x7F) == 0x7E)     # saturated to +-448
+
+
 ALL_PINS = [
     pin_golden_worked_examples,
     pin_golden_bf16_rounding,
@@ -379,6 +402,7 @@ ALL_PINS = [
     pin_headwise_constant_heads,
     pin_headwise_heads_independent,
     pin_headwise_top_level,
+    pin_fp8_top_level,
 ]
 
 assert oracle.qknorm_fused is oq.qknorm_fused

@@ -15,6 +15,7 @@ from oracle import qknorm as oq
 from oracle_pins import ALL_PINS
 
 _orig_shard = oq.shard_sum_of_squares
+_orig_fp8 = oq.f64_to_fp8_bits
 _orig_round = obf16.f64_to_bf16_bits
 
 
@@ -136,6 +137,8 @@ MUTANTS = {
     "decode_bf16_shift15": ("bf16_bits_to_f64", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)),
     "q_k_gamma_swapped": ("qknorm_fused", _fused_gamma_swapped),
     "q_k_normalized_jointly": ("qknorm_fused", _fused_joint),
+    "fp8_gamma_read_as_fp8": ("decode_gamma", lambda a, dtype: oq.decode_input(a, dtype)),
+    "fp8_output_not_saturated": ("f64_to_fp8_bits", lambda v: np.where(np.abs(np.asarray(v)) > 464, np.uint8(0x7F), _orig_fp8(v)).astype(np.uint8)),
     "headwise_one_factor_per_row": ("headwise_rmsnorm", _headwise_as_layerwise),
     "headwise_gamma_always_shared": ("headwise_rmsnorm", _headwise_stride("shared")),
     "headwise_gamma_always_per_column": ("headwise_rmsnorm", _headwise_stride("full")),
