@@ -53,6 +53,8 @@ def to_device(a, dev):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(dev)
     return torch.from_numpy(a.copy()).to(dev)
 
 
@@ -73,15 +75,16 @@ class FusedStep:
             y = torch.zeros_like(x0)
             self.sets.append((x, y))
         esz = x0.element_size()
+        gsz = inp.gamma_q.dtype.itemsize   # bf16 gamma for FP8 rows
         if w.head_dim:   # headwise: one shared [head_dim] gamma per tensor
             self.gq = to_device(inp.gamma_q[:w.head_dim], dev)
             self.gk = to_device(inp.gamma_k[:w.head_dim], dev)
-            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + 2 * w.head_dim * esz
+            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + 2 * w.head_dim * gsz
             self.name = "qknorm_headwise"
         else:
             self.gq = to_device(inp.gamma_q, dev)
             self.gk = to_device(inp.gamma_k, dev)
-            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+            self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * gsz
             self.name = "qknorm_fused"
         self.footprint = self.n_sets * per_set
         self.launches = 1
@@ -124,9 +127,10 @@ class SplitStep:
         self.gq = to_device(inp.gamma_q, dev)
         self.gk = to_device(inp.gamma_k, dev)
         esz = x0.element_size()
+        gsz = inp.gamma_q.dtype.itemsize
         h = w.hq + w.hk
         self.bytes_partial = w.T * h * esz + 8 * w.T
-        self.bytes_apply = 2 * w.T * h * esz + 8 * (1 + P) * w.T + h * esz
+        self.bytes_apply = 2 * w.T * h * esz + 8 * (1 + P) * w.T + h * gsz
         self.bytes = self.bytes_partial + self.bytes_apply
         self.footprint = self.n_sets * per_set
         self.launches = 2
@@ -286,8 +290,9 @@ def record_traffic(workload, d_fetch, d_write, d_copy_fetch, d_copy_write, copy_
     f_scale = copy_bytes / (med["copy_fetch"] * 1024.0)
     w_scale = copy_bytes / (med["copy_write"] * 1024.0)
     w = I.WORKLOADS[workload]
-    esz = 2 if w.dtype == "bf16" else 4
-    algo = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+    esz = {"bf16": 2, "f32": 4, "fp8": 1}[w.dtype]
+    gsz = 4 if w.dtype == "f32" else 2
+    algo = 2 * w.T * (w.hq + w.hk) * esz + ((2 * w.head_dim) if w.head_dim else (w.hq + w.hk)) * gsz
     traffic = med["fetch"] * 1024.0 * f_scale + med["write"] * 1024.0 * w_scale
     out = {
         "workload": workload,

@@ -27,9 +27,12 @@
  *   - partial[s] = float32 sum of x_j^2 over shard s, in a fixed order that
  *     depends only on the shapes, the shard count and T;
  *   - sum = ((partial[0] + partial[1]) + ...) + partial[S-1]   (float32);
- *   - r = rsqrt(sum / H + eps)                                    (float32);
- *   - y_j = (x_j * gamma_j) * r, rounded once to the I/O type (bf16: round
- *     to nearest even).
+ *   - m = fma(sum, 1/H, eps), with 1/H rounded once to float32 on the host;
+ *   - r = reciprocal square root of m from the hardware's float32 rsqrt
+ *     (within about one float32 ulp; m below the float32 normal range is
+ *     scaled by 2^64 first and r by 2^32 after, keeping that accuracy);
+ *   - y_j = (x_j * gamma_j) * r, rounded once to the I/O type (bf16 and FP8:
+ *     round to nearest even; FP8 saturates to +-448).
  *   The float32 accumulation is the paper's (Fig. 2(b) accumulates squared
  *   sums in FP32 for BF16 activations); rows whose sum of squares overflows
  *   float32 (|x| around 1e19) give 0 or NaN instead of the real result.
@@ -75,7 +78,7 @@
 extern "C" {
 #endif
 
-#define QKNORM_ABI_VERSION 2
+#define QKNORM_ABI_VERSION 3
 
 /* Largest shard count and number of statistic planes accepted. */
 #define QKNORM_MAX_SHARDS 64
@@ -84,8 +87,13 @@ extern "C" {
 #define QKNORM_MAX_FULL_WIDTH (1 << 24)
 
 typedef enum qknorm_dtype {
-  QKNORM_F32 = 0,  /* float32 I/O */
-  QKNORM_BF16 = 1  /* bfloat16 I/O, float32 arithmetic */
+  QKNORM_F32 = 0,      /* float32 rows and gamma */
+  QKNORM_BF16 = 1,     /* bfloat16 rows and gamma, float32 arithmetic */
+  QKNORM_FP8_E4M3 = 2  /* FP8 E4M3 rows (OCP E4M3FN: bias 7, max 448, NaN 0x7F/0xFF,
+                          no infinity), bfloat16 gamma, float32 arithmetic. Outputs are
+                          rounded to nearest even and saturated to +-448; NaN stays NaN.
+                          Fig. 2(b) of the paper evaluates FP8-E4M3 activations with
+                          FP32 accumulation. */
 } qknorm_dtype_t;
 
 typedef enum qknorm_status {
@@ -110,7 +118,8 @@ typedef struct qknorm_operand {
                         is in place; any other overlap with an input or output is rejected.
                         Not used by qknorm_partial_stats (may be NULL there). */
   int64_t ld_y;      /* output row stride in elements, >= h (ignored by qknorm_partial_stats) */
-  const void* gamma; /* h per-column scales, I/O type (not used by qknorm_partial_stats) */
+  const void* gamma; /* h per-column scales: the row type, bf16 for FP8 rows
+                        (not used by qknorm_partial_stats) */
   int64_t h;         /* local width: number of columns normalized, > 0 */
 } qknorm_operand_t;
 
@@ -122,7 +131,8 @@ typedef struct qknorm_operand {
  *
  *   q, k    operand descriptors (host pointers to structs holding device pointers)
  *   T       tokens (rows), >= 0
- *   dtype   QKNORM_F32 or QKNORM_BF16, for x, y and gamma alike
+ *   dtype   QKNORM_F32, QKNORM_BF16 (x, y and gamma alike) or QKNORM_FP8_E4M3
+ *           (x and y FP8, gamma bf16)
  *   eps     finite, >= 0
  *   shards  S in [1, QKNORM_MAX_SHARDS]; q->h % S == 0 and k->h % S == 0
  *   stream  hipStream_t or NULL
@@ -182,7 +192,7 @@ int qknorm_apply_with_stats(const qknorm_operand_t* q, const qknorm_operand_t* k
  *   q, k, T, dtype, eps, stream as for qknorm_fused (gamma holds
  *   (heads - 1) * stride + head_dim elements).
  *
- * Heads of up to 4096 bf16 / 2048 fp32 elements and up to 256 heads per
+ * Heads of up to 4096 bf16 / 2048 fp32 / 8192 FP8 elements and up to 256 heads per
  * token (Q and K together) are supported; larger ones return
  * QKNORM_ERR_UNSUPPORTED.
  */

@@ -18,14 +18,18 @@ _LIB_PATH = os.path.join(_HERE, "libqknorm.so")
 
 QKNORM_F32 = 0
 QKNORM_BF16 = 1
+QKNORM_FP8_E4M3 = 2
 QKNORM_OK = 0
 QKNORM_ERR_INVALID_ARG = 1
 QKNORM_ERR_UNSUPPORTED = 2
 QKNORM_ERR_HIP = 3
 OP_FUSED, OP_PARTIAL_STATS, OP_APPLY_WITH_STATS = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 EXPORTS = ("qknorm_fused", "qknorm_partial_stats", "qknorm_apply_with_stats", "qknorm_headwise",
            "qknorm_last_error", "qknorm_abi_version", "qknorm_describe_plan", "qknorm_describe_headwise_plan")
+
+
+_DTYPES = {"f32": (QKNORM_F32, 4), "bf16": (QKNORM_BF16, 2), "fp8": (QKNORM_FP8_E4M3, 1)}
 
 
 class QKNormError(RuntimeError):
@@ -103,7 +107,15 @@ def _dtype_code(t):
         return QKNORM_BF16
     if t.dtype == torch.float32:
         return QKNORM_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype == torch.float8_e4m3fn:
+        return QKNORM_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float32 or float8_e4m3fn)")
+
+
+def _gamma_dtype(x):
+    """gamma is bf16 for FP8 rows, the row dtype otherwise."""
+    import torch
+    return torch.bfloat16 if x.dtype == torch.float8_e4m3fn else x.dtype
 
 
 def _rows(t, name):
@@ -132,8 +144,8 @@ def _operand(x, y, gamma, name):
     if gamma is not None:
         if gamma.dim() != 1 or gamma.shape[0] != x.shape[1] or (gamma.shape[0] > 1 and gamma.stride(0) != 1):
             raise ValueError(f"gamma for {name} must be contiguous [{x.shape[1]}]")
-        if gamma.dtype != x.dtype:
-            raise TypeError(f"gamma for {name} must have dtype {x.dtype}")
+        if gamma.dtype != _gamma_dtype(x):
+            raise TypeError(f"gamma for {name} must have dtype {_gamma_dtype(x)}")
         op.gamma = gamma.data_ptr()
     return op
 
@@ -225,8 +237,8 @@ def qknorm_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, 
     ok = _operand(k, out_k, None, "k")
     for g, o, name in ((gamma_q, oq, "q"), (gamma_k, ok, "k")):
         need = (o.h // head_dim - 1) * gamma_head_stride + head_dim if head_dim > 0 else 0
-        if g.dim() != 1 or g.shape[0] < need or (g.shape[0] > 1 and g.stride(0) != 1) or g.dtype != q.dtype:
-            raise ValueError(f"gamma for {name} must be contiguous, dtype {q.dtype}, >= {need} elements")
+        if g.dim() != 1 or g.shape[0] < need or (g.shape[0] > 1 and g.stride(0) != 1) or g.dtype != _gamma_dtype(q):
+            raise ValueError(f"gamma for {name} must be contiguous, dtype {_gamma_dtype(q)}, >= {need} elements")
         o.gamma = g.data_ptr()
     _check(lib.qknorm_headwise(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), int(head_dim),
                                int(gamma_head_stride), _stream(q, stream)))
@@ -236,8 +248,7 @@ def qknorm_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, 
 def describe_headwise_plan(hq, hk, T, head_dim, dtype="bf16", gamma_head_stride=0, ld=None):
     """The launch qknorm_headwise would make, for shapes alone (no GPU needed)."""
     lib = load_library()
-    code = QKNORM_BF16 if dtype == "bf16" else QKNORM_F32
-    esz = 2 if dtype == "bf16" else 4
+    code, esz = _DTYPES[dtype]
     ld = ld if ld is not None else hq + hk
     xq, xk = (1 << 32), (1 << 32) + hq * esz if ld >= hq + hk else (1 << 40)
     oq = Operand(xq, ld, xq + (1 << 44), ld, 1 << 46, hq)
@@ -254,8 +265,7 @@ def describe_plan(op, hq, hk, T, dtype="bf16", shards=1, ld=None, aligned=True):
     Uses stand-in addresses for a packed layout (never dereferenced).
     """
     lib = load_library()
-    code = QKNORM_BF16 if dtype == "bf16" else QKNORM_F32
-    esz = 2 if dtype == "bf16" else 4
+    code, esz = _DTYPES[dtype]
     ld = ld if ld is not None else hq + hk
     off = 0 if aligned else esz
     if ld >= hq + hk:      # packed rows: K follows Q in the same rows

@@ -40,8 +40,12 @@ int ok() {
 size_t elem_size(int dtype) {
   if (dtype == QKNORM_F32) return 4;
   if (dtype == QKNORM_BF16) return 2;
+  if (dtype == QKNORM_FP8_E4M3) return 1;
   return 0;
 }
+
+// gamma is bf16 for FP8 rows, the row type otherwise
+size_t gamma_size(int dtype) { return dtype == QKNORM_F32 ? 4 : 2; }
 
 // The set of bytes touched by rows t < T, columns j < h of a strided matrix.
 struct Region {
@@ -159,7 +163,7 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   for (int c = 0; c < 2; ++c) {
     xr[c] = Region{(uintptr_t)ops[c]->x, ops[c]->ld_x, ops[c]->h, T, e};
     yr[c] = Region{(uintptr_t)ops[c]->y, ops[c]->ld_y, ops[c]->h, T, e};
-    gr[c] = Region{(uintptr_t)ops[c]->gamma, ops[c]->h, ops[c]->h, 1, e};
+    gr[c] = Region{(uintptr_t)ops[c]->gamma, ops[c]->h, ops[c]->h, 1, (int64_t)gamma_size(dtype)};
   }
   if (mode != qkn::MODE_STATS) {
     if (may_overlap(yr[0], yr[1])) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k outputs overlap", fn);
@@ -197,7 +201,7 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   }
 
   std::string why;
-  if (!qkn::make_plan(mode, dtype == QKNORM_BF16, aligned, shards, q->h, k->h, T, &out->plan, &why))
+  if (!qkn::make_plan(mode, dtype, aligned, shards, q->h, k->h, T, &out->plan, &why))
     return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
 
   qkn::RowArgs& a = out->args;
@@ -222,8 +226,14 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   a.group = out->plan.group;
   a.tok_threads = out->plan.tok_threads;
   a.tokens_per_block = out->plan.tokens_per_block;
-  a.divq = (float)(mode == qkn::MODE_APPLY ? hq_full : q->h);
-  a.divk = (float)(mode == qkn::MODE_APPLY ? hk_full : k->h);
+  a.inv_divq = (float)(1.0 / (double)(mode == qkn::MODE_APPLY ? hq_full : q->h));
+  a.inv_divk = (float)(1.0 / (double)(mode == qkn::MODE_APPLY ? hk_full : k->h));
+  a.log2_lanes = 0;
+  while ((1 << a.log2_lanes) < a.lanes) ++a.log2_lanes;
+  a.log2_group = 0;
+  while ((1 << a.log2_group) < out->plan.group) ++a.log2_group;
+  a.groups_per_shard = out->plan.lanes / out->plan.group;
+  a.groups_per_token = out->plan.tok_threads / out->plan.group;
   a.eps = eps;
   a.partials = mode == qkn::MODE_STATS ? (float*)stat_buf : nullptr;
   a.stats = mode == qkn::MODE_APPLY ? (const float*)stat_buf : nullptr;
@@ -278,7 +288,7 @@ int check_and_plan_heads(const qknorm_operand_t* q, const qknorm_operand_t* k, i
     xr[c] = Region{(uintptr_t)ops[c]->x, ops[c]->ld_x, ops[c]->h, T, e};
     yr[c] = Region{(uintptr_t)ops[c]->y, ops[c]->ld_y, ops[c]->h, T, e};
     const int64_t gext = (heads - 1) * gstride + head_dim;  // gamma elements read
-    gr[c] = Region{(uintptr_t)ops[c]->gamma, gext, gext, 1, e};
+    gr[c] = Region{(uintptr_t)ops[c]->gamma, gext, gext, 1, (int64_t)gamma_size(dtype)};
   }
   if (may_overlap(yr[0], yr[1])) return fail(QKNORM_ERR_INVALID_ARG, "%s: q and k outputs overlap", fn);
   for (int c = 0; c < 2; ++c) {
@@ -298,7 +308,7 @@ int check_and_plan_heads(const qknorm_operand_t* q, const qknorm_operand_t* k, i
               o->ld_x % vw == 0 && o->ld_y % vw == 0;
   }
   std::string why;
-  if (!qkn::make_head_plan(dtype == QKNORM_BF16, aligned, head_dim, q->h / head_dim, k->h / head_dim, T, &out->plan,
+  if (!qkn::make_head_plan(dtype, aligned, head_dim, q->h / head_dim, k->h / head_dim, T, &out->plan,
                            &why))
     return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   qkn::HeadArgs& a = out->args;
@@ -322,7 +332,9 @@ int check_and_plan_heads(const qknorm_operand_t* q, const qknorm_operand_t* k, i
   a.lanes = out->plan.lanes;
   a.tok_threads = out->plan.tok_threads;
   a.tokens_per_block = out->plan.tokens_per_block;
-  a.div = (float)head_dim;
+  a.inv_div = (float)(1.0 / (double)head_dim);
+  a.log2_nc = 0;
+  while ((1 << a.log2_nc) < out->plan.ncq) ++a.log2_nc;
   a.eps = eps;
   return QKNORM_OK;
 }
@@ -351,13 +363,13 @@ static int slots_for(int v) {
 // many waves share the work of a token and the loads of many tokens overlap;
 // idle slots waste issue slots, so layouts that leave more than 1/8 of the
 // slots empty are avoided when another layout fits.
-bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* p, std::string* why) {
   Plan r;
   r.mode = mode;
-  r.bf16 = bf16 ? 1 : 0;
+  r.dtype = dtype;
   r.aligned = aligned ? 1 : 0;
-  r.vw = bf16 ? 8 : 4;
+  r.vw = chunk_elems(dtype);
   r.shards = shards;
   const int64_t hq_s = hq / shards, hk_s = hk / shards;
   const int64_t max_chunks = (int64_t)kMaxThreads * 8;  // per token: 1024 threads x 8 slots
@@ -388,9 +400,10 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
     const int g = shards * l;
     if (g % 64 || g > kMaxThreads) return 0;
     const int v = slots_for(ceil_div(nc, l));
-    return (v && g <= max_threads_for_slots(v)) ? v : 0;
+    return (v && g <= max_threads_for_slots(v, dtype)) ? v : 0;
   };
   for (int l = kMinLanesPerShard; l <= kMaxThreads; l = l < 64 ? l * 2 : l + 64) {
+    if (shards > 1 && (l & (l - 1))) continue;  // several shards: power-of-two lane groups only
     const int v = fits_block(l);
     if (!v) continue;
     const int g = shards * l;
@@ -418,7 +431,7 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
   r.waves = r.tok_threads / 64;
   // One-wave tokens are packed four to a block; wider tokens get a block each.
   r.tokens_per_block = (r.waves == 1 && !few_tokens) ? 4 : 1;
-  if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots)) r.tokens_per_block = 1;
+  if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots, dtype)) r.tokens_per_block = 1;
   r.threads = r.tokens_per_block * r.tok_threads;
   const int groups_per_token = r.tok_threads / r.group;
   r.lds_bytes = r.waves > 1 ? 2 * r.tokens_per_block * groups_per_token * 2 * (int)sizeof(float) : 0;
@@ -429,13 +442,13 @@ bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_
 // Headwise launch geometry: the same rule as the layerwise planner (about 3
 // chunks per lane, few idle slots; few tokens: fewer chunks per lane), with
 // a group of L lanes per head and blocks of about 512 threads.
-bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
+bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
                     Plan* p, std::string* why) {
   Plan r;
   r.mode = MODE_HEADWISE;
-  r.bf16 = bf16 ? 1 : 0;
+  r.dtype = dtype;
   r.aligned = aligned ? 1 : 0;
-  r.vw = bf16 ? 8 : 4;
+  r.vw = chunk_elems(dtype);
   const int64_t nc = (head_dim + r.vw - 1) / r.vw;
   const int64_t heads = heads_q + heads_k;
   if (nc > 64 * 8) {
@@ -464,7 +477,7 @@ bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, 
     double best_score = 1e30;
     for (int g = 64; g <= kMaxThreads; g += 64) {
       const int v = slots_for((int)((total + g - 1) / g));
-      if (!v || g > max_threads_for_slots(v)) continue;
+      if (!v || g > max_threads_for_slots(v, dtype)) continue;
       const double wfrac = (double)((int64_t)g * v - total) / (double)(g * v);
       const double score = few_tokens
           ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
@@ -482,7 +495,7 @@ bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, 
       r.slots = best_v;
       r.tok_threads = best_g;
       r.tokens_per_block = (best_g == 64 && !few_tokens) ? 4 : 1;
-      if (r.tokens_per_block * best_g > max_threads_for_slots(best_v)) r.tokens_per_block = 1;
+      if (r.tokens_per_block * best_g > max_threads_for_slots(best_v, dtype)) r.tokens_per_block = 1;
       r.threads = r.tokens_per_block * best_g;
       r.waves = r.threads / 64;
       *p = r;
@@ -497,7 +510,7 @@ bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, 
     if (!v) continue;
     const int64_t g = heads * l;
     const int64_t threads = (g + 63) / 64 * 64;
-    if (threads > max_threads_for_slots(v)) continue;
+    if (threads > max_threads_for_slots(v, dtype)) continue;
     const double wfrac = (double)((int64_t)l * v - nc) / (double)(l * v);
     const double score = few_tokens
         ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
@@ -518,7 +531,7 @@ bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, 
   r.tok_threads = (int)heads * best_l;
   int tpb = few_tokens ? 1 : (int)(512 / r.tok_threads);
   if (tpb < 1) tpb = 1;
-  while (tpb > 1 && (tpb * r.tok_threads + 63) / 64 * 64 > max_threads_for_slots(best_v)) --tpb;
+  while (tpb > 1 && (tpb * r.tok_threads + 63) / 64 * 64 > max_threads_for_slots(best_v, dtype)) --tpb;
   r.tokens_per_block = tpb;
   r.threads = (tpb * r.tok_threads + 63) / 64 * 64;
   r.waves = r.threads / 64;
@@ -526,13 +539,15 @@ bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, 
   return true;
 }
 
+static const char* dtype_name(int d) { return d == kDtypeF32 ? "f32" : d == kDtypeBF16 ? "bf16" : "fp8_e4m3"; }
+
 std::string describe(const Plan& p) {
   if (p.mode == MODE_HEADWISE) {
     char buf[320];
     snprintf(buf, sizeof buf,
              "headwise %s path=%s layout=%s heads=(%d,%d) head_dim=%d chunks/head=%d lanes/head=%d "
              "threads/token=%d tokens/block=%d threads/block=%d slots=%d",
-             p.bf16 ? "bf16" : "f32", p.aligned ? "16B" : "elementwise", p.heads_packed ? "token-wide" : "per-head",
+             dtype_name(p.dtype), p.aligned ? "16B" : "elementwise", p.heads_packed ? "token-wide" : "per-head",
              p.heads_q, p.heads_k, p.head_dim, p.ncq, p.heads_packed ? p.ncq : p.lanes, p.tok_threads,
              p.tokens_per_block, p.threads, p.slots);
     return buf;
@@ -542,7 +557,7 @@ std::string describe(const Plan& p) {
            "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads/token=%d "
            "tokens/block=%d waves/token=%d slots=%d lds=%d",
            p.mode == MODE_FUSED ? "fused" : p.mode == MODE_STATS ? "partial_stats" : "apply_with_stats",
-           p.bf16 ? "bf16" : "f32", p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
+           dtype_name(p.dtype), p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
            p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
   return buf;
 }

@@ -10,6 +10,14 @@ namespace qkn {
 
 enum Mode : int { MODE_FUSED = 0, MODE_STATS = 1, MODE_APPLY = 2, MODE_HEADWISE = 3 };
 
+// I/O types (the values of qknorm_dtype_t).
+enum Dtype : int { kDtypeF32 = 0, kDtypeBF16 = 1, kDtypeFP8 = 2 };
+
+// Elements per 16-byte chunk, bytes per row element, bytes per gamma element.
+constexpr int chunk_elems(int dtype) { return dtype == kDtypeF32 ? 4 : dtype == kDtypeBF16 ? 8 : 16; }
+constexpr int row_elem_bytes(int dtype) { return dtype == kDtypeF32 ? 4 : dtype == kDtypeBF16 ? 2 : 1; }
+constexpr int gamma_elem_bytes(int dtype) { return dtype == kDtypeF32 ? 4 : 2; }
+
 // Chunk-slot counts per lane that have a compiled kernel.
 constexpr int kSlotSizes[] = {1, 2, 3, 4, 6, 8, 12, 16};
 constexpr int kMaxSlots = 16;
@@ -17,9 +25,10 @@ constexpr int kMaxThreads = 1024;   // threads working on one token (one block)
 constexpr int kMinLanesPerShard = 4;
 
 // Largest block that a kernel with `v` chunk slots per lane is compiled for.
-// Up to 8 slots the data and gamma fit the 128 VGPRs a 1024-thread block
-// allows; 12 and 16 slots need more, so those kernels take at most 256.
-constexpr int max_threads_for_slots(int v) { return v <= 8 ? kMaxThreads : 256; }
+// Up to 8 slots (3 for FP8 rows, whose bf16 gamma takes twice the registers
+// of the data) the data and gamma fit the 128 VGPRs a 1024-thread block
+// allows; more slots need more, so those kernels take at most 256 threads.
+constexpr int max_threads_for_slots(int v, int dtype) { return v <= (dtype == 2 ? 3 : 8) ? kMaxThreads : 256; }
 
 // How one token's Q and K columns are spread over a block.
 //
@@ -33,7 +42,7 @@ constexpr int max_threads_for_slots(int v) { return v <= 8 ? kMaxThreads : 256; 
 // block holds `tokens_per_block` such tokens side by side.
 struct Plan {
   int mode = 0;
-  int bf16 = 1;       // 1: bf16 I/O, 0: fp32 I/O
+  int dtype = kDtypeBF16;
   int aligned = 0;    // 1: 16-byte loads/stores; 0: element-wise path
   int vw = 8;         // elements per chunk
   int shards = 1;     // S
@@ -71,7 +80,10 @@ struct RowArgs {
   int ncq, nck;
   int shards;
   int lanes, group, tok_threads, tokens_per_block;
-  float divq, divk;   // H for Q and K in Eq. 1
+  int log2_lanes;     // log2(lanes) when shards > 1 (lanes is then a power of two)
+  int log2_group;     // log2(group)
+  int groups_per_shard, groups_per_token;
+  float inv_divq, inv_divk;  // 1/H for Q and K in Eq. 1, rounded once
   float eps;
   float* partials;    // MODE_STATS: [S][2][T]
   const float* stats; // MODE_APPLY: [P][2][T]
@@ -99,19 +111,20 @@ struct HeadArgs {
                       // token-wide layout: nc (the lane group of one head)
   int tok_threads;    // threads per token
   int tokens_per_block;
-  float div;          // head_dim, the H of Eq. 1
+  int log2_nc;        // token-wide layout: log2(nc)
+  float inv_div;      // 1/head_dim, rounded once (H of Eq. 1)
   float eps;
 };
 
 // Plans a headwise launch; false (with a reason) if no kernel holds a head.
-bool make_head_plan(bool bf16, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
+bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, int64_t heads_k, int64_t T,
                     Plan* plan, std::string* why);
 
 int launch_heads(const Plan& plan, const HeadArgs& args, void* stream, std::string* err);
 
 // Fills `plan` for the given shapes; returns false (with a reason) if no
 // compiled kernel can hold the row.
-bool make_plan(int mode, bool bf16, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* plan, std::string* why);
 
 std::string describe(const Plan& p);

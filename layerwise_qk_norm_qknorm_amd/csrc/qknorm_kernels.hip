@@ -36,37 +36,81 @@
 namespace qkn {
 namespace {
 
+// I/O types. kVW: elements per 16-byte row chunk; kBytes: bytes per row
+// element; kGW / kGBytes: 32-bit words of gamma per chunk and bytes per gamma
+// element (FP8 rows take bf16 gamma).
 struct BF16 {
-  static constexpr int kVW = 8;  // elements per 16-byte chunk
-  static constexpr int kBytes = 2;
+  static constexpr int kVW = 8, kBytes = 2, kGW = 4, kGBytes = 2, kDtype = kDtypeBF16;
 };
 struct F32 {
-  static constexpr int kVW = 4;
-  static constexpr int kBytes = 4;
+  static constexpr int kVW = 4, kBytes = 4, kGW = 4, kGBytes = 4, kDtype = kDtypeF32;
+};
+struct FP8 {  // OCP FP8 E4M3 (E4M3FN) rows, bf16 gamma
+  static constexpr int kVW = 16, kBytes = 1, kGW = 8, kGBytes = 2, kDtype = kDtypeFP8;
 };
 
-struct Chunk {
-  uint32_t w[4];
+template <int W>
+struct Words {
+  uint32_t w[W];
 };
+using Chunk = Words<4>;  // 16 bytes of row data
+template <class IO>
+using GChunk = Words<IO::kGW>;  // the gamma of one chunk
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Element e of a chunk as float32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// All elements of a row chunk as float32 (exact widening).
 template <class IO>
-__device__ __forceinline__ float elem(const Chunk& c, int e);
+__device__ __forceinline__ void decode(const Chunk& c, float (&v)[IO::kVW]);
 template <>
-__device__ __forceinline__ float elem<BF16>(const Chunk& c, int e) {
-  const uint32_t w = c.w[e >> 1];
-  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+__device__ __forceinline__ void decode<BF16>(const Chunk& c, float (&v)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    v[2 * p] = bf16_lo(c.w[p]);
+    v[2 * p + 1] = bf16_hi(c.w[p]);
+  }
 }
 template <>
-__device__ __forceinline__ float elem<F32>(const Chunk& c, int e) {
-  return __uint_as_float(c.w[e]);
+__device__ __forceinline__ void decode<F32>(const Chunk& c, float (&v)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) v[p] = __uint_as_float(c.w[p]);
+}
+template <>
+__device__ __forceinline__ void decode<FP8>(const Chunk& c, float (&v)[16]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // v_cvt_pk_f32_fp8: two E4M3 values of one 16-bit half per instruction
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(c.w[p], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(c.w[p], true);
+    v[4 * p] = lo[0];
+    v[4 * p + 1] = lo[1];
+    v[4 * p + 2] = hi[0];
+    v[4 * p + 3] = hi[1];
+  }
 }
 
-// Packs float32 results into a chunk of the I/O type (bf16: round to nearest even).
+// The gamma of a chunk as float32 (exact).
+template <class IO>
+__device__ __forceinline__ void decode_gamma(const GChunk<IO>& g, float (&v)[IO::kVW]) {
+  if (IO::kGBytes == 2) {
+#pragma unroll
+    for (int p = 0; p < IO::kGW; ++p) {
+      v[2 * p] = bf16_lo(g.w[p]);
+      v[2 * p + 1] = bf16_hi(g.w[p]);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < IO::kGW; ++p) v[p] = __uint_as_float(g.w[p]);
+  }
+}
+
+// float32 results -> a chunk of the I/O type, one rounding to nearest even.
+// For FP8 the caller saturates to +-448 first where needed (sat_e4m3; NaN
+// stays NaN): the hardware conversion turns magnitudes past 464 into NaN.
 template <class IO>
 __device__ __forceinline__ void pack(Chunk& c, const float (&v)[IO::kVW]);
 template <>
@@ -82,41 +126,65 @@ __device__ __forceinline__ void pack<F32>(Chunk& c, const float (&v)[4]) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) c.w[p] = __float_as_uint(v[p]);
 }
+__device__ __forceinline__ float sat_e4m3(float x) { return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x); }
+template <>
+__device__ __forceinline__ void pack<FP8>(Chunk& c, const float (&v)[16]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * p], v[4 * p + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * p + 2], v[4 * p + 3], w, true);
+    c.w[p] = (uint32_t)w;
+  }
+}
 
-// Loads a chunk at element offset `col` of row `row`: all kVW elements on the
-// 16-byte path (which requires a 16-byte aligned address), the first `n`
-// (1 <= n <= kVW) on the element-wise path, where elements past `n` read as 0.
+// Loads `W` words at `p`: 16-byte loads (p 16-byte aligned) on the aligned
+// path; on the element-wise path the first `n` elements of `esz` bytes, the
+// rest reading as 0.
 //
 // Every load is unconditional: a lane whose slot is idle passes the row's
 // first chunk (always a valid address) and its value is masked by the caller.
 // Predicated loads would put each load in its own branch with a wait for it
 // before the join, leaving one load in flight per wave.
-template <class IO, bool ALIGNED>
-__device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
-  Chunk c = {{0u, 0u, 0u, 0u}};
-  const char* p = row + (int64_t)col * IO::kBytes;
-  if (ALIGNED) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    c.w[0] = v.x;
-    c.w[1] = v.y;
-    c.w[2] = v.z;
-    c.w[3] = v.w;
-  } else if (IO::kBytes == 2) {
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+template <int W, int ESZ, bool ALIGNED>
+__device__ __forceinline__ Words<W> load_words(const char* p, int n) {
+  Words<W> c;
 #pragma unroll
-    for (int e = 0; e < IO::kVW; ++e) {
-      const uint32_t v = s[e < n ? e : 0];
-      c.w[e >> 1] |= (e < n ? v : 0u) << ((e & 1) * 16);
+  for (int q = 0; q < W; ++q) c.w[q] = 0u;
+  if (ALIGNED) {
+#pragma unroll
+    for (int q = 0; q < W; q += 4) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + 4 * q);
+      c.w[q] = v.x;
+      c.w[q + 1] = v.y;
+      c.w[q + 2] = v.z;
+      c.w[q + 3] = v.w;
     }
   } else {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+    constexpr int kElems = W * 4 / ESZ;
 #pragma unroll
-    for (int e = 0; e < IO::kVW; ++e) {
-      const uint32_t v = s[e < n ? e : 0];
-      c.w[e] = e < n ? v : 0u;
+    for (int e = 0; e < kElems; ++e) {
+      const int ee = e < n ? e : 0;
+      uint32_t v;
+      if (ESZ == 1) v = reinterpret_cast<const uint8_t*>(p)[ee];
+      else if (ESZ == 2) v = reinterpret_cast<const uint16_t*>(p)[ee];
+      else v = reinterpret_cast<const uint32_t*>(p)[ee];
+      c.w[(e * ESZ) / 4] |= (e < n ? v : 0u) << (((e * ESZ) % 4) * 8);
     }
   }
   return c;
+}
+
+// The chunk at element offset `col` of row `row` (the first `n` elements on
+// the element-wise path).
+template <class IO, bool ALIGNED>
+__device__ __forceinline__ Chunk load_chunk(const char* row, int col, int n) {
+  return load_words<4, IO::kBytes, ALIGNED>(row + (int64_t)col * IO::kBytes, n);
+}
+
+// The gamma of the chunk at column `col`, from gamma base `base`.
+template <class IO, bool ALIGNED>
+__device__ __forceinline__ GChunk<IO> load_gamma(const char* base, int col, int n) {
+  return load_words<IO::kGW, IO::kGBytes, ALIGNED>(base + (int64_t)col * IO::kGBytes, n);
 }
 
 // Stores the first `n` elements of a chunk. Results are written once and not
@@ -128,44 +196,106 @@ __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chu
   if (ALIGNED) {
     const u32x4_t v = {c.w[0], c.w[1], c.w[2], c.w[3]};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
-  } else if (IO::kBytes == 2) {
-    uint16_t* d = reinterpret_cast<uint16_t*>(p);
-#pragma unroll
-    for (int e = 0; e < IO::kVW; ++e)
-      if (e < n) d[e] = (uint16_t)(c.w[e >> 1] >> ((e & 1) * 16));
   } else {
-    uint32_t* d = reinterpret_cast<uint32_t*>(p);
 #pragma unroll
-    for (int e = 0; e < IO::kVW; ++e)
-      if (e < n) d[e] = c.w[e];
+    for (int e = 0; e < IO::kVW; ++e) {
+      if (e < n) {
+        const uint32_t v = c.w[(e * IO::kBytes) / 4] >> (((e * IO::kBytes) % 4) * 8);
+        if (IO::kBytes == 1) reinterpret_cast<uint8_t*>(p)[e] = (uint8_t)v;
+        else if (IO::kBytes == 2) reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)v;
+        else reinterpret_cast<uint32_t*>(p)[e] = v;
+      }
+    }
   }
 }
 
 // Sum of squares of one chunk, in element order (Phase A, in-lane part).
 template <class IO>
 __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
+  float v[IO::kVW];
+  decode<IO>(c, v);
   float s = 0.0f;
 #pragma unroll
-  for (int e = 0; e < IO::kVW; ++e) {
-    const float x = elem<IO>(c, e);
-    s = __builtin_fmaf(x, x, s);
-  }
+  for (int e = 0; e < IO::kVW; ++e) s = __builtin_fmaf(v[e], v[e], s);
   return s;
 }
 
-// RMS factor of Eq. 1 for a global squared sum `ss` over full width `div`:
-// 1 / sqrt(ss / div + eps), each step correctly rounded in float32 (it runs
-// once per token, so the exact forms cost nothing measurable).
-__device__ __forceinline__ float rms_factor(float ss, float div, float eps) {
-  return 1.0f / __builtin_sqrtf(ss / div + eps);
+// Phase B and the final scaling for this lane's chunks of one token:
+// y = (x * gamma) * r[i], one rounding to the I/O type, stores of the valid
+// chunks (slot i goes to the Q or the K row). For FP8 the saturating
+// conversion costs four operations per element, so with up to 4 slots the
+// wave first checks whether any result exceeds 448 in magnitude (NaN results
+// need no clamp: they convert to NaN) and clamps only then.
+template <class IO, int V, bool ALIGNED>
+__device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<IO> (&g)[V], const float (&r)[V],
+                                            const bool (&isq)[V], const int (&col)[V], const int (&cnt)[V],
+                                            char* yq_row, char* yk_row, bool active) {
+  constexpr int VW = IO::kVW;
+  if (IO::kDtype == kDtypeFP8 && V <= 4) {
+    float y[V][VW];
+    float big = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float xf[VW], gf[VW];
+      decode<IO>(xv[i], xf);
+      decode_gamma<IO>(g[i], gf);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        y[i][e] = (xf[e] * gf[e]) * r[i];
+        if (cnt[i] > 0) big = __builtin_fmaxf(big, __builtin_fabsf(y[i][e]));
+      }
+    }
+    const bool clamp = __builtin_amdgcn_ballot_w64(active && big > 448.0f) != 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (clamp) {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) y[i][e] = sat_e4m3(y[i][e]);
+      }
+      Chunk out;
+      pack<IO>(out, y[i]);
+      if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (active && cnt[i] > 0) {
+        float xf[VW], gf[VW], y[VW];
+        decode<IO>(xv[i], xf);
+        decode_gamma<IO>(g[i], gf);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+          y[e] = (xf[e] * gf[e]) * r[i];
+          if (IO::kDtype == kDtypeFP8) y[e] = sat_e4m3(y[e]);  // many slots: clamp unconditionally
+        }
+        Chunk out;
+        pack<IO>(out, y);
+        store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+      }
+    }
+  }
 }
 
-// Register-pressure guard: an empty asm that claims to rewrite the four words
-// of `c`. Values the compiler decoded from them earlier (bf16 -> float32
-// widenings) can then not be kept alive across this point and are decoded
-// again where they are used, so a chunk costs 4 VGPRs instead of 8.
-__device__ __forceinline__ void keep_packed(Chunk& c) {
-  asm volatile("" : "+v"(c.w[0]), "+v"(c.w[1]), "+v"(c.w[2]), "+v"(c.w[3]));
+// RMS factor of Eq. 1 for a global squared sum `ss`, full width H given as
+// inv_div = 1/H (rounded once on the host): r = rsq(fma(ss, 1/H, eps)) with
+// the hardware reciprocal square root (1 ulp). Arguments below the normal
+// range are scaled by 2^64 first, so the result stays accurate there too;
+// 0 gives +inf and +inf gives 0, as the formula does.
+__device__ __forceinline__ float rms_factor(float ss, float inv_div, float eps) {
+  const float m = __builtin_fmaf(ss, inv_div, eps);
+  const bool tiny = m < 1.17549435e-38f;  // false for NaN
+  const float r = __builtin_amdgcn_rsqf(tiny ? m * 0x1p64f : m);
+  return tiny ? r * 0x1p32f : r;
+}
+
+// Register-pressure guard: empty asm statements that claim to rewrite the
+// words of `c`. Values the compiler widened from them earlier (bf16 or fp8 ->
+// float32) can then not be kept alive across this point and are widened
+// again where they are used, so packed data stays packed in registers.
+template <int W>
+__device__ __forceinline__ void keep_packed(Words<W>& c) {
+#pragma unroll
+  for (int q = 0; q < W; ++q) asm volatile("" : "+v"(c.w[q]));
 }
 
 // Sum over aligned groups of `group` lanes (a power of two, 1..64); every
@@ -195,16 +325,20 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 }
 
 template <class IO, int V, int MODE, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const RowArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_rows(const RowArgs a) {
   extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token][2]
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
   const int L = a.lanes;
-  const int j = tid / G;          // token slot within the block
-  const int r = tid - j * G;      // thread within the token
-  const int s = r / L;            // shard group
-  const int m = r - s * L;        // lane within the group
+  // Tokens share a block only when each takes one wave, and shards share a
+  // token only with power-of-two lane groups, so the lane decomposition is
+  // shifts and masks.
+  const int j = a.tokens_per_block > 1 ? tid >> 6 : 0;   // token slot within the block
+  const int r = a.tokens_per_block > 1 ? tid & 63 : tid;  // thread within the token
+  const int s = a.shards > 1 ? r >> a.log2_lanes : 0;     // shard group
+  const int m = a.shards > 1 ? r & (L - 1) : r;           // lane within the group
+  const int qbase = __umul24(s, a.hq_s), kbase = __umul24(s, a.hk_s);
 
   // Token-invariant geometry of this lane's chunk slots.
   bool isq[V];
@@ -216,13 +350,13 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
     if (u < a.ncq) {
       const int c = u * VW;
       isq[i] = true;
-      col[i] = s * a.hq_s + c;
-      cnt[i] = min(VW, a.hq_s - c);
+      col[i] = qbase + c;
+      cnt[i] = ALIGNED ? VW : min(VW, a.hq_s - c);
     } else if (u < a.ncq + a.nck) {
       const int c = (u - a.ncq) * VW;
       isq[i] = false;
-      col[i] = s * a.hk_s + c;
-      cnt[i] = min(VW, a.hk_s - c);
+      col[i] = kbase + c;
+      cnt[i] = ALIGNED ? VW : min(VW, a.hk_s - c);
     } else {  // idle slot: reads (and ignores) the first chunk of the Q row
       isq[i] = true;
       col[i] = 0;
@@ -230,16 +364,16 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
     }
   }
 
-  Chunk g[MODE == MODE_STATS ? 1 : V];
+  GChunk<IO> g[MODE == MODE_STATS ? 1 : V];
   if (MODE != MODE_STATS) {
 #pragma unroll
     for (int i = 0; i < V; ++i)
-      g[i] = load_chunk<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], max(cnt[i], 1));
+      g[i] = load_gamma<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], max(cnt[i], 1));
   }
 
   const int group = a.group;            // butterfly width: min(L, 64)
-  const int gps = L / group;            // groups per shard
-  const int gpt = G / group;            // groups per token
+  const int gps = a.groups_per_shard;   // L / group
+  const int gpt = a.groups_per_token;   // G / group
   const int tpb = a.tokens_per_block;
   const int64_t step = (int64_t)gridDim.x * tpb;
   int buf = 0;
@@ -256,7 +390,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
     Chunk xv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
-    if (MODE != MODE_STATS && IO::kBytes == 2) {
+    if (MODE != MODE_STATS && IO::kBytes < 4) {
 #pragma unroll
       for (int i = 0; i < V; ++i) keep_packed(g[i]);
     }
@@ -294,8 +428,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
         // by iteration, so one barrier per iteration suffices).
         float* rb = red + ((buf * tpb + j) * gpt) * 2;
         if ((r & (group - 1)) == 0) {
-          rb[(r / group) * 2 + 0] = aq;
-          rb[(r / group) * 2 + 1] = ak;
+          rb[(r >> a.log2_group) * 2 + 0] = aq;
+          rb[(r >> a.log2_group) * 2 + 1] = ak;
         }
         __syncthreads();
         if (MODE == MODE_STATS) {
@@ -331,27 +465,19 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
       }
     }
 
-    if (MODE != MODE_STATS && active) {
-      if (IO::kBytes == 2) {
+    if constexpr (MODE != MODE_STATS) {
+      if (IO::kBytes < 4 && V > 4) {  // at most 4 slots stay widened in registers
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
-      const float rq = rms_factor(ssq, a.divq, a.eps);
-      const float rk = rms_factor(ssk, a.divk, a.eps);
-      char* yq_row = static_cast<char*>(a.yq) + t * a.ldyq * IO::kBytes;
-      char* yk_row = static_cast<char*>(a.yk) + t * a.ldyk * IO::kBytes;
+      const float rq = rms_factor(ssq, a.inv_divq, a.eps);
+      const float rk = rms_factor(ssk, a.inv_divk, a.eps);
+      float rr[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        if (cnt[i] > 0) {
-          const float rr = isq[i] ? rq : rk;
-          float y[VW];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
-          Chunk out;
-          pack<IO>(out, y);
-          store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
-        }
-      }
+      for (int i = 0; i < V; ++i) rr[i] = isq[i] ? rq : rk;
+      char* yq_row = static_cast<char*>(a.yq) + tr * a.ldyq * IO::kBytes;
+      char* yk_row = static_cast<char*>(a.yk) + tr * a.ldyk * IO::kBytes;
+      scale_store<IO, V, ALIGNED>(xv, g, rr, isq, col, cnt, yq_row, yk_row, active);
     }
   }
 }
@@ -364,7 +490,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_rows(const Ro
 // needed. Blocks are rounded up to whole waves; lanes past the last token
 // slot only read valid addresses and write nothing.
 template <class IO, int V, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const HeadArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_heads(const HeadArgs a) {
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
@@ -393,15 +519,15 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const H
     }
   }
   // this head's gamma (head * stride elements in; the first head's for stride 0)
-  const char* gbase = static_cast<const char*>(isq ? a.gq : a.gk) + (int64_t)head * a.gstride * IO::kBytes;
+  const char* gbase = static_cast<const char*>(isq ? a.gq : a.gk) + (int64_t)head * a.gstride * IO::kGBytes;
   const char* xbase = static_cast<const char*>(isq ? a.xq : a.xk);
   char* ybase = static_cast<char*>(isq ? a.yq : a.yk);
   const int64_t ldx = isq ? a.ldxq : a.ldxk;
   const int64_t ldy = isq ? a.ldyq : a.ldyk;
 
-  Chunk g[V];
+  GChunk<IO> g[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) g[i] = load_chunk<IO, ALIGNED>(gbase, gcol[i], max(cnt[i], 1));
+  for (int i = 0; i < V; ++i) g[i] = load_gamma<IO, ALIGNED>(gbase, gcol[i], max(cnt[i], 1));
 
   const int tpb = a.tokens_per_block;
   const int64_t step = (int64_t)gridDim.x * tpb;
@@ -414,7 +540,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const H
     Chunk xv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(x_row, col[i], max(cnt[i], 1));
-    if (IO::kBytes == 2) {
+    if (IO::kBytes < 4) {
 #pragma unroll
       for (int i = 0; i < V; ++i) keep_packed(g[i]);
     }
@@ -423,24 +549,21 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const H
     for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
     acc = group_sum(acc, L);
 
-    if (active) {
-      if (IO::kBytes == 2) {
+    {
+      if (IO::kBytes < 4 && V > 4) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
-      const float rr = rms_factor(acc, a.div, a.eps);
-      char* y_row = ybase + t * ldy * IO::kBytes;
+      const float f = rms_factor(acc, a.inv_div, a.eps);
+      float rr[V];
+      bool isqv[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        if (cnt[i] > 0) {
-          float y[VW];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
-          Chunk out;
-          pack<IO>(out, y);
-          store_chunk<IO, ALIGNED>(y_row, col[i], cnt[i], out);
-        }
+        rr[i] = f;
+        isqv[i] = true;
       }
+      char* y_row = ybase + tr * ldy * IO::kBytes;
+      scale_store<IO, V, ALIGNED>(xv, g, rr, isqv, col, cnt, y_row, y_row, active);
     }
   }
 }
@@ -453,13 +576,13 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads(const H
 // consecutive lanes of a slot hold exactly one head: each slot is reduced
 // over its aligned nc-lane group and scaled by that head's factor.
 template <class IO, int V, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(const HeadArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_heads_packed(const HeadArgs a) {
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;                 // lanes per token, a multiple of 64 and of nc
   const int nc = a.lanes;                      // chunks per head (power of two, <= 64)
-  const int j = tid / G;                       // token slot within the block
-  const int m = tid - j * G;
+  const int j = a.tokens_per_block > 1 ? tid >> 6 : 0;  // token slot (several only with G = 64)
+  const int m = a.tokens_per_block > 1 ? tid & 63 : tid;
   const int total = (a.heads_q + a.heads_k) * nc;
 
   bool isq[V];
@@ -469,13 +592,13 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(
   for (int i = 0; i < V; ++i) {
     const int u = i * G + m;
     if (u < total) {
-      const int head = u / nc;
-      const int c = (u - head * nc) * VW;
+      const int head = u >> a.log2_nc;
+      const int c = (u & (nc - 1)) * VW;
       isq[i] = head < a.heads_q;
       const int hh = isq[i] ? head : head - a.heads_q;
-      col[i] = hh * a.head_dim + c;
-      cnt[i] = min(VW, a.head_dim - c);
-      gp[i] = static_cast<const char*>(isq[i] ? a.gq : a.gk) + ((int64_t)hh * a.gstride + c) * IO::kBytes;
+      col[i] = __umul24(hh, a.head_dim) + c;
+      cnt[i] = ALIGNED ? VW : min(VW, a.head_dim - c);
+      gp[i] = static_cast<const char*>(isq[i] ? a.gq : a.gk) + ((int64_t)hh * a.gstride + c) * IO::kGBytes;
     } else {  // idle slot: reads (and ignores) the first chunk of the Q row and of gamma
       isq[i] = true;
       col[i] = 0;
@@ -483,9 +606,9 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(
       gp[i] = static_cast<const char*>(a.gq);
     }
   }
-  Chunk g[V];
+  GChunk<IO> g[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) g[i] = load_chunk<IO, ALIGNED>(gp[i], 0, max(cnt[i], 1));
+  for (int i = 0; i < V; ++i) g[i] = load_gamma<IO, ALIGNED>(gp[i], 0, max(cnt[i], 1));
 
   const int tpb = a.tokens_per_block;
   const int64_t step = (int64_t)gridDim.x * tpb;
@@ -498,7 +621,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(
     Chunk xv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
-    if (IO::kBytes == 2) {
+    if (IO::kBytes < 4) {
 #pragma unroll
       for (int i = 0; i < V; ++i) keep_packed(g[i]);
     }
@@ -506,25 +629,17 @@ __global__ void __launch_bounds__(max_threads_for_slots(V)) qknorm_heads_packed(
 #pragma unroll
     for (int i = 0; i < V; ++i) ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
 
-    if (active) {
-      if (IO::kBytes == 2) {
+    {
+      if (IO::kBytes < 4 && V > 4) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
-      char* yq_row = static_cast<char*>(a.yq) + t * a.ldyq * IO::kBytes;
-      char* yk_row = static_cast<char*>(a.yk) + t * a.ldyk * IO::kBytes;
+      float rr[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        if (cnt[i] > 0) {
-          const float rr = rms_factor(ss[i], a.div, a.eps);
-          float y[VW];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) y[e] = (elem<IO>(xv[i], e) * elem<IO>(g[i], e)) * rr;
-          Chunk out;
-          pack<IO>(out, y);
-          store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
-        }
-      }
+      for (int i = 0; i < V; ++i) rr[i] = rms_factor(ss[i], a.inv_div, a.eps);
+      char* yq_row = static_cast<char*>(a.yq) + tr * a.ldyq * IO::kBytes;
+      char* yk_row = static_cast<char*>(a.yk) + tr * a.ldyk * IO::kBytes;
+      scale_store<IO, V, ALIGNED>(xv, g, rr, isq, col, cnt, yq_row, yk_row, active);
     }
   }
 }
@@ -588,10 +703,22 @@ HeadKernelFn pick_head_io(const Plan& p) {
   return p.aligned ? pick_head_slots<IO, true, false>(p.slots) : pick_head_slots<IO, false, false>(p.slots);
 }
 
-HeadKernelFn pick_head_kernel(const Plan& p) { return p.bf16 ? pick_head_io<BF16>(p) : pick_head_io<F32>(p); }
+HeadKernelFn pick_head_kernel(const Plan& p) {
+  switch (p.dtype) {
+    case kDtypeBF16: return pick_head_io<BF16>(p);
+    case kDtypeF32: return pick_head_io<F32>(p);
+    case kDtypeFP8: return pick_head_io<FP8>(p);
+  }
+  return nullptr;
+}
 
 KernelFn pick_kernel(const Plan& p) {
-  return p.bf16 ? pick_mode<BF16>(p.mode, p.aligned, p.slots) : pick_mode<F32>(p.mode, p.aligned, p.slots);
+  switch (p.dtype) {
+    case kDtypeBF16: return pick_mode<BF16>(p.mode, p.aligned, p.slots);
+    case kDtypeF32: return pick_mode<F32>(p.mode, p.aligned, p.slots);
+    case kDtypeFP8: return pick_mode<FP8>(p.mode, p.aligned, p.slots);
+  }
+  return nullptr;
 }
 
 }  // namespace

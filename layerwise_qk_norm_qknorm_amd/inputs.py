@@ -41,7 +41,7 @@ class Workload:
     hq: int
     hk: int
     hv: int
-    dtype: str                 # "bf16" or "f32"
+    dtype: str                 # "bf16", "f32" or "fp8" (FP8 E4M3 rows, bf16 gamma)
     packed: bool
     shards: tuple              # shard counts S exercised by the fused call
     x_dist: str = "normal"     # normal | normal_token_scale | normal_outliers
@@ -81,7 +81,17 @@ GQA_PREFILL_HEADWISE = replace(GQA_PREFILL, key="gqa_prefill_headwise",
                                title="GQA prefill, headwise: T=8192, 40+8 heads of 128, bf16 packed [8192, 7168]",
                                head_dim=128)
 
-WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE, GQA_PREFILL_HEADWISE)}
+# The same shapes with FP8 E4M3 activations (bf16 gamma), the paper's second
+# precision in Fig. 2(b).
+GQA_PREFILL_FP8 = replace(GQA_PREFILL, key="gqa_prefill_fp8",
+                          title="GQA prefill, FP8 E4M3: T=8192, fp8 packed [8192, 7168], bf16 gamma, S=1",
+                          dtype="fp8")
+RANK_SLICE_FP8 = replace(RANK_SLICE, key="rank_slice_fp8",
+                         title="Rank slice, FP8 E4M3: T=16384, local 1280/256 of 5120/1024, fp8 packed [16384, 1792]",
+                         dtype="fp8")
+
+WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE, GQA_PREFILL_HEADWISE,
+                                GQA_PREFILL_FP8, RANK_SLICE_FP8)}
 
 
 def _rng(cfg_id, stream):
@@ -96,13 +106,30 @@ def to_bf16_bits(a):
     return u.astype(np.uint16)
 
 
+def to_fp8_bits(a):
+    """float64 -> float32 -> FP8 E4M3 (E4M3FN) bit patterns, nearest even, via
+    torch's float8_e4m3fn cast. Data must stay within +-448."""
+    import torch
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    if np.abs(f).max(initial=0.0) > 448:
+        raise ValueError("FP8 E4M3 inputs must lie within +-448")
+    return torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
 def to_io(a, dtype):
-    """Convert float64 draws to the I/O representation (bf16 bits or float32)."""
+    """Convert float64 draws to the I/O representation (bf16 bits, float32 or FP8 bits)."""
     if dtype == "bf16":
         return to_bf16_bits(a)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float64).astype(np.float32)
+    if dtype == "fp8":
+        return to_fp8_bits(a)
     raise ValueError(dtype)
+
+
+def gamma_dtype(dtype):
+    """gamma is bf16 for FP8 rows, the row type otherwise."""
+    return "bf16" if dtype == "fp8" else dtype
 
 
 def _gamma(dist, rng, n):
@@ -145,8 +172,8 @@ def make_inputs(w: Workload) -> Inputs:
         meta["n_outliers"] = int(mask.sum())
     elif w.x_dist != "normal":
         raise ValueError(w.x_dist)
-    gq = to_io(_gamma(w.gamma_dist, _rng(w.cfg_id, STREAM_GQ), hq), w.dtype)
-    gk = to_io(_gamma(w.gamma_dist, _rng(w.cfg_id, STREAM_GK), hk), w.dtype)
+    gq = to_io(_gamma(w.gamma_dist, _rng(w.cfg_id, STREAM_GQ), hq), gamma_dtype(w.dtype))
+    gk = to_io(_gamma(w.gamma_dist, _rng(w.cfg_id, STREAM_GK), hk), gamma_dtype(w.dtype))
 
     if w.packed:
         v = _rng(w.cfg_id, STREAM_V).standard_normal((T, w.hv))

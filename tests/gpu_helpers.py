@@ -13,10 +13,13 @@ GUARD = 4096  # bytes of canary before and after every device buffer
 
 
 def np_to_torch(a):
-    """numpy uint16 (bf16 bits) or float32 -> CPU torch tensor of the I/O dtype."""
+    """numpy uint16 (bf16 bits), uint8 (FP8 E4M3 bits) or float32 -> CPU torch
+    tensor of the I/O dtype."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a.copy()).view(torch.float8_e4m3fn)
     if a.dtype == np.float32:
         return torch.from_numpy(a.copy())
     raise TypeError(a.dtype)
@@ -26,6 +29,8 @@ def torch_to_np(t):
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     if t.dtype == torch.float32:
         return t.numpy().copy()
     raise TypeError(t.dtype)
@@ -45,7 +50,7 @@ class Guarded:
         rng = np.random.default_rng(seed)
         total = self.offset + self.n + ge
         canary = rng.integers(0, 1 << (8 * esz), total, dtype=np.uint64).astype(
-            np.uint16 if esz == 2 else np.uint32)
+            {1: np.uint8, 2: np.uint16, 4: np.uint32}[esz])
         if esz == 4:
             canary = canary.view(np.float32)
             # keep canaries finite so that equality checks are plain
@@ -121,3 +126,27 @@ def fig2b_errors(got64, gold64):
     d = np.abs(np.asarray(got64, np.float64) - np.asarray(gold64, np.float64))
     d = d[np.isfinite(d)]
     return float(d.max()), float(d.mean()), float(np.sqrt(np.mean(d * d)))
+
+
+def fp8_order(bits):
+    """Monotone integer for FP8 E4M3 patterns: adjacent values differ by 1, +0 == -0."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7F
+    return np.where(b & 0x80, -mag, mag)
+
+
+def check_fp8(got_bits, want_bits, what=""):
+    """|order(got) - order(want)| <= 1 everywhere; NaN (0x7F/0xFF) exactly where
+    the oracle has NaN. Returns (exact-match fraction, max step difference)."""
+    got_bits = np.asarray(got_bits, np.uint8)
+    want_bits = np.asarray(want_bits, np.uint8)
+    assert got_bits.shape == want_bits.shape
+    gnan = (got_bits & 0x7F) == 0x7F
+    wnan = (want_bits & 0x7F) == 0x7F
+    assert np.array_equal(gnan, wnan), f"{what}: NaN positions differ ({gnan.sum()} vs {wnan.sum()})"
+    ok = ~wnan
+    d = np.abs(fp8_order(got_bits[ok]) - fp8_order(want_bits[ok]))
+    dmax = int(d.max()) if d.size else 0
+    if dmax > 1:
+        raise AssertionError(f"{what}: {int((d > 1).sum())} elements beyond 1 FP8 step, max {dmax}")
+    return (float((d == 0).mean()) if d.size else 1.0), dmax

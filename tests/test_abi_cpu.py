@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert qk.abi_version() == 2
+    assert qk.abi_version() == 3
 
 
 # stand-in addresses: packed rows, outputs elsewhere
@@ -238,3 +238,19 @@ def test_headwise_plans():
     with pytest.raises(qk.QKNormError) as e:
         qk.describe_headwise_plan(257 * 8, 8, 4, 8)         # more heads than a block holds
     assert e.value.status == UNSUPPORTED
+
+
+def test_fp8_plans_and_checks():
+    # FP8 rows: 16 elements per 16-byte chunk; GQA prefill is 384 chunks per token
+    d = qk.describe_plan(OP_FUSED, 5120, 1024, 8192, "fp8", 1, ld=7168)
+    assert "fp8_e4m3" in d and "chunks=(320,64)" in d and "slots=3" in d and "path=16B" in d
+    d = qk.describe_plan(OP_FUSED, 5120, 1024, 8192, "fp8", 1, ld=7176)
+    assert "elementwise" in d                              # row stride not a multiple of 16
+    d = qk.describe_headwise_plan(5120, 1024, 8192, 128, "fp8", ld=7168)
+    assert "chunks/head=8" in d and "layout=token-wide" in d
+    q, k = ops(hq=256, hk=128, esz=1)
+    buf = ctypes.create_string_buffer(256)
+    lib = qk.load_library()
+    assert lib.qknorm_describe_plan(OP_FUSED, ctypes.byref(q), ctypes.byref(k), 16, 2, 1, buf, 256) == 0
+    q.y = q.x + 1                                          # partial in-place shift by one FP8 element
+    assert fused(q, k, dtype=2) == INVALID

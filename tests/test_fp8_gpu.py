@@ -1,0 +1,169 @@
+"""GPU parity for FP8 E4M3 rows (OCP E4M3FN) with bf16 gamma and fp32
+arithmetic: every call against the float64 oracle, element by element.
+Acceptance: each FP8 output is the oracle's once-rounded (saturating) E4M3
+result or one of its two neighbours; NaN exactly where the oracle has NaN;
+V columns and guard bands untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import layerwise_qk_norm_qknorm_amd as qk
+from layerwise_qk_norm_qknorm_amd import inputs as I
+from gpu_helpers import DEV, Guarded, check_fp8, fig2b_errors, np_to_torch, torch_to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qk.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layout(inp, hv, ld_pad=0, offset=0, seed=0):
+    """Packed host rows [T, hq + hk + hv + ld_pad] and guarded device copies."""
+    w = inp.workload
+    T, hq, hk = inp.q.shape[0], inp.q.shape[1], inp.k.shape[1]
+    ld = hq + hk + hv + ld_pad
+    host = np.zeros((T, ld), np.uint8)
+    host[:, :hq] = inp.q
+    host[:, hq:hq + hk] = inp.k
+    if hv + ld_pad:
+        host[:, hq + hk:] = np.random.default_rng(seed).integers(0, 0x7F, (T, hv + ld_pad)).astype(np.uint8)
+    src = Guarded(host, seed=seed, offset_elems=offset)
+    dst = Guarded(np.random.default_rng(seed + 9).integers(0, 0x7F, host.shape).astype(np.uint8), seed=seed + 1,
+                  offset_elems=offset)
+    return host, src, dst
+
+
+def _compare(got, ref, what):
+    hq = ref.yq.shape[1]
+    eq, _ = check_fp8(got[:, :hq], ref.yq_bits, what + " Q")
+    ek, _ = check_fp8(got[:, hq:hq + ref.yk.shape[1]], ref.yk_bits, what + " K")
+    gold = oracle.fp8_bits_to_f64(got[:, :hq])
+    e = fig2b_errors(gold, ref.yq)
+    _log(f"[parity] {what}: exact FP8 match Q {eq:.5f} K {ek:.5f}; vs fp64 gold Q max/mean/rms "
+         f"{e[0]:.3g}/{e[1]:.3g}/{e[2]:.3g}")
+
+
+def _untouched(host, src, dst, dst_init, hq, hk):
+    assert src.guards_intact() and dst.guards_intact()
+    assert np.array_equal(src.host(), host)
+    assert np.array_equal(dst.host()[:, hq + hk:], dst_init[:, hq + hk:])
+
+
+def _fused(inp, hv, shards, eps=1e-6, **kw):
+    hq, hk = inp.q.shape[1], inp.k.shape[1]
+    host, src, dst = _layout(inp, hv, **kw)
+    dst_init = dst.host()
+    x, y = src.view(), dst.view()
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], gq, gk, eps, shards, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    out = dst.host()
+    _untouched(host, src, dst, dst_init, hq, hk)
+    return out, oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", eps, shards)
+
+
+def test_gqa_prefill_fp8_full_size():
+    w = I.GQA_PREFILL_FP8
+    _log(f"[case] {w.key} plan: {qk.describe_plan(0, w.hq, w.hk, w.T, 'fp8', 1, ld=w.ld)}")
+    inp = I.make_inputs(w)
+    out, ref = _fused(inp, w.hv, 1)
+    _compare(out, ref, w.key)
+
+
+@pytest.mark.parametrize("T", [1, 64, 256])
+@pytest.mark.parametrize("shards", [1, 8])
+def test_decode_fp8(T, shards):
+    inp = I.make_custom(T, 4096, 4096, 0, "fp8", seed=600 + T)
+    out, ref = _fused(inp, 4096, shards)
+    _compare(out, ref, f"decode fp8 T={T} S={shards}")
+
+
+def test_rank_slice_fp8_partial_and_apply():
+    w = I.RANK_SLICE_FP8
+    inp = I.make_inputs(w)
+    hq, hk = w.hq, w.hk
+    host, src, dst = _layout(inp, w.hv)
+    dst_init = dst.host()
+    x, y = src.view(), dst.view()
+    part = qk.qknorm_partial_stats(x[:, :hq], x[:, hq:hq + hk], 1).cpu().numpy().astype(np.float64)
+    ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "fp8", 1)
+    assert np.all(np.abs(part - ref_p) <= 1e-5 * ref_p)
+    planes = [ref_p[0]] + [oracle.qknorm_partial_stats(inp.peer_q[p], inp.peer_k[p], "fp8", 1)[0]
+                           for p in range(inp.peer_q.shape[0])]
+    planes = np.stack(planes).astype(np.float32)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    qk.qknorm_apply_with_stats(x[:, :hq], x[:, hq:hq + hk], gq, gk, w.eps, torch.from_numpy(planes).to(DEV),
+                               w.hq_full, w.hk_full, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", w.eps, planes,
+                                         w.hq_full, w.hk_full)
+    _compare(dst.host(), ref, "rank_slice_fp8 apply")
+    _untouched(host, src, dst, dst_init, hq, hk)
+
+
+def test_fused_equals_split_fp8_bitwise():
+    inp = I.make_custom(300, 2048, 512, 0, "fp8", seed=701)
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    fq, fk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 4, fq, fk)
+    part = qk.qknorm_partial_stats(xq, xk, 4)
+    aq, ak = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, part, 2048, 512, aq, ak)
+    torch.cuda.synchronize()
+    assert torch.equal(fq.view(torch.uint8), aq.view(torch.uint8))
+    assert torch.equal(fk.view(torch.uint8), ak.view(torch.uint8))
+
+
+def test_headwise_fp8():
+    w = I.GQA_PREFILL_FP8.with_T(1024)
+    inp = I.make_inputs(w)
+    hq, hk = w.hq, w.hk
+    host, src, dst = _layout(inp, w.hv)
+    dst_init = dst.host()
+    x, y = src.view(), dst.view()
+    gq_h, gk_h = inp.gamma_q[:128].copy(), inp.gamma_k[:128].copy()
+    qk.qknorm_headwise(x[:, :hq], x[:, hq:hq + hk], np_to_torch(gq_h).to(DEV), np_to_torch(gk_h).to(DEV), w.eps, 128,
+                       0, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_headwise(inp.q, inp.k, gq_h, gk_h, "fp8", w.eps, 128, 0)
+    _compare(dst.host(), ref, "headwise fp8")
+    _untouched(host, src, dst, dst_init, hq, hk)
+
+
+def test_fp8_saturates_instead_of_nan():
+    """gamma of 300 pushes many results past 448: they must come out as +-448."""
+    inp = I.make_custom(64, 512, 128, 0, "fp8", seed=801)
+    inp.gamma_q[...] = I.to_bf16_bits(np.full(512, 300.0))
+    out, ref = _fused(inp, 0, 1)
+    big = np.abs(ref.yq) > 464
+    assert big.sum() > 1000
+    assert np.all((out[:, :512][big] & 0x7F) == 0x7E)
+    _compare(out, ref, "fp8 saturation")
+
+
+def test_fp8_elementwise_path():
+    _compare(*_fused(I.make_custom(45, 40 * 8, 24, 0, "fp8", seed=901), 8, 1, offset=3), "fp8 misaligned")
+    _compare(*_fused(I.make_custom(31, 1000, 200, 0, "fp8", seed=902), 0, 4, ld_pad=1), "fp8 odd stride")
+    _compare(*_fused(I.make_custom(19, 120, 24, 0, "fp8", seed=903), 16, 3), "fp8 shard of 40")
+
+
+def test_fp8_nan_rows():
+    inp = I.make_custom(8, 256, 64, 0, "fp8", seed=1001)
+    inp.q[3, 7] = 0x7F      # NaN: the whole Q row of token 3 becomes NaN
+    inp.k[5, 0] = 0xFF
+    out, ref = _fused(inp, 0, 1)
+    assert np.all((out[3, :256] & 0x7F) == 0x7F) and np.all((out[5, 256:320] & 0x7F) == 0x7F)
+    _compare(out, ref, "fp8 NaN rows")

@@ -47,3 +47,13 @@ def test_bf16_input_rounding_is_nearest():
     v = np.array([1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9, -2.5, 0.1])
     b = I.to_bf16_bits(v)
     assert list(b) == [0x3F80, 0x3F81, 0xC020, 0x3DCD]
+
+
+def test_fp8_inputs():
+    w = I.GQA_PREFILL_FP8.with_T(64)
+    inp = I.make_inputs(w)
+    assert inp.qkv.dtype == np.uint8 and inp.gamma_q.dtype == np.uint16      # FP8 rows, bf16 gamma
+    from oracle.fp8 import fp8_bits_to_f64
+    x = fp8_bits_to_f64(inp.qkv[:, :6144])
+    assert np.isfinite(x).all() and np.abs(x).max() <= 448
+    assert np.array_equal(I.to_fp8_bits(np.array([1.0, -2.5, 448.0, 1.0625])), np.array([0x38, 0xC2, 0x7E, 0x38]))
