@@ -352,9 +352,10 @@ namespace qkn {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-static int slots_for(int v) {
+// Smallest compiled slot count >= v, or 0 if it exceeds `max`.
+static int slots_for(int v, int max) {
   for (int s : kSlotSizes)
-    if (s >= v) return s;
+    if (s >= v) return s <= max ? s : 0;
   return 0;
 }
 
@@ -399,8 +400,8 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   auto fits_block = [&](int l) {
     const int g = shards * l;
     if (g % 64 || g > kMaxThreads) return 0;
-    const int v = slots_for(ceil_div(nc, l));
-    return (v && g <= max_threads_for_slots(v, dtype)) ? v : 0;
+    const int v = slots_for(ceil_div(nc, l), max_slots(dtype, aligned));
+    return (v && g <= max_threads_for_slots(v, dtype, aligned)) ? v : 0;
   };
   for (int l = kMinLanesPerShard; l <= kMaxThreads; l = l < 64 ? l * 2 : l + 64) {
     if (shards > 1 && (l & (l - 1))) continue;  // several shards: power-of-two lane groups only
@@ -431,7 +432,7 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   r.waves = r.tok_threads / 64;
   // One-wave tokens are packed four to a block; wider tokens get a block each.
   r.tokens_per_block = (r.waves == 1 && !few_tokens) ? 4 : 1;
-  if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots, dtype)) r.tokens_per_block = 1;
+  if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots, dtype, aligned)) r.tokens_per_block = 1;
   r.threads = r.tokens_per_block * r.tok_threads;
   const int groups_per_token = r.tok_threads / r.group;
   r.lds_bytes = r.waves > 1 ? 2 * r.tokens_per_block * groups_per_token * 2 * (int)sizeof(float) : 0;
@@ -476,8 +477,8 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
     int best_g = 0, best_v = 0;
     double best_score = 1e30;
     for (int g = 64; g <= kMaxThreads; g += 64) {
-      const int v = slots_for((int)((total + g - 1) / g));
-      if (!v || g > max_threads_for_slots(v, dtype)) continue;
+      const int v = slots_for((int)((total + g - 1) / g), max_slots(dtype, aligned));
+      if (!v || g > max_threads_for_slots(v, dtype, aligned)) continue;
       const double wfrac = (double)((int64_t)g * v - total) / (double)(g * v);
       const double score = few_tokens
           ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
@@ -495,7 +496,7 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
       r.slots = best_v;
       r.tok_threads = best_g;
       r.tokens_per_block = (best_g == 64 && !few_tokens) ? 4 : 1;
-      if (r.tokens_per_block * best_g > max_threads_for_slots(best_v, dtype)) r.tokens_per_block = 1;
+      if (r.tokens_per_block * best_g > max_threads_for_slots(best_v, dtype, aligned)) r.tokens_per_block = 1;
       r.threads = r.tokens_per_block * best_g;
       r.waves = r.threads / 64;
       *p = r;
@@ -506,11 +507,11 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
   int best_l = 0, best_v = 0;
   double best_score = 1e30;
   for (int l = kMinLanesPerShard; l <= 64; l *= 2) {
-    const int v = slots_for(ceil_div((int)nc, l));
+    const int v = slots_for(ceil_div((int)nc, l), max_slots(dtype, aligned));
     if (!v) continue;
     const int64_t g = heads * l;
     const int64_t threads = (g + 63) / 64 * 64;
-    if (threads > max_threads_for_slots(v, dtype)) continue;
+    if (threads > max_threads_for_slots(v, dtype, aligned)) continue;
     const double wfrac = (double)((int64_t)l * v - nc) / (double)(l * v);
     const double score = few_tokens
         ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
@@ -531,7 +532,7 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
   r.tok_threads = (int)heads * best_l;
   int tpb = few_tokens ? 1 : (int)(512 / r.tok_threads);
   if (tpb < 1) tpb = 1;
-  while (tpb > 1 && (tpb * r.tok_threads + 63) / 64 * 64 > max_threads_for_slots(best_v, dtype)) --tpb;
+  while (tpb > 1 && (tpb * r.tok_threads + 63) / 64 * 64 > max_threads_for_slots(best_v, dtype, aligned)) --tpb;
   r.tokens_per_block = tpb;
   r.threads = (tpb * r.tok_threads + 63) / 64 * 64;
   r.waves = r.threads / 64;

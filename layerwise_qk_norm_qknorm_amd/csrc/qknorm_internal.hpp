@@ -25,10 +25,18 @@ constexpr int kMaxThreads = 1024;   // threads working on one token (one block)
 constexpr int kMinLanesPerShard = 4;
 
 // Largest block that a kernel with `v` chunk slots per lane is compiled for.
-// Up to 8 slots (3 for FP8 rows, whose bf16 gamma takes twice the registers
-// of the data) the data and gamma fit the 128 VGPRs a 1024-thread block
-// allows; more slots need more, so those kernels take at most 256 threads.
-constexpr int max_threads_for_slots(int v, int dtype) { return v <= (dtype == 2 ? 3 : 8) ? kMaxThreads : 256; }
+// A 1024-thread block leaves each lane 128 VGPRs. On the 16-byte path that
+// holds the data and gamma of up to 8 slots (3 for FP8 rows, whose bf16
+// gamma takes twice the registers of the data); the element-wise path keeps
+// one register per element in flight, so it fits fewer (6 fp32, 4 bf16, 1
+// FP8). Kernels with more slots take at most 256 threads (512 VGPRs).
+constexpr int max_threads_for_slots(int v, int dtype, bool aligned) {
+  return v <= (aligned ? (dtype == 2 ? 3 : 8) : (dtype == 0 ? 6 : dtype == 1 ? 4 : 1)) ? kMaxThreads : 256;
+}
+
+// Most chunk slots per lane with a compiled kernel. Element-wise FP8 rows stop
+// at 8: 12 or 16 slots of single-byte loads need more than 512 VGPRs.
+constexpr int max_slots(int dtype, bool aligned) { return (dtype == 2 && !aligned) ? 8 : kMaxSlots; }
 
 // How one token's Q and K columns are spread over a block.
 //

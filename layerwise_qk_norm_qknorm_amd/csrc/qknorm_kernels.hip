@@ -325,7 +325,7 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 }
 
 template <class IO, int V, int MODE, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_rows(const RowArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_rows(const RowArgs a) {
   extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token][2]
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_r
 // needed. Blocks are rounded up to whole waves; lanes past the last token
 // slot only read valid addresses and write nothing.
 template <class IO, int V, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_heads(const HeadArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_heads(const HeadArgs a) {
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
@@ -576,7 +576,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_h
 // consecutive lanes of a slot hold exactly one head: each slot is reduced
 // over its aligned nc-lane group and scaled by that head's factor.
 template <class IO, int V, bool ALIGNED>
-__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype)) qknorm_heads_packed(const HeadArgs a) {
+__global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_heads_packed(const HeadArgs a) {
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;                 // lanes per token, a multiple of 64 and of nc
@@ -658,8 +658,10 @@ KernelFn pick_slots(int v) {
     case 4: return qknorm_rows<IO, 4, MODE, ALIGNED>;
     case 6: return qknorm_rows<IO, 6, MODE, ALIGNED>;
     case 8: return qknorm_rows<IO, 8, MODE, ALIGNED>;
-    case 12: return qknorm_rows<IO, 12, MODE, ALIGNED>;
-    case 16: return qknorm_rows<IO, 16, MODE, ALIGNED>;
+  }
+  if constexpr (max_slots(IO::kDtype, ALIGNED) == kMaxSlots) {
+    if (v == 12) return qknorm_rows<IO, 12, MODE, ALIGNED>;
+    if (v == 16) return qknorm_rows<IO, 16, MODE, ALIGNED>;
   }
   return nullptr;
 }
@@ -689,8 +691,10 @@ HeadKernelFn pick_head_slots(int v) {
     case 4: return QKN_HEAD_KERNEL(4);
     case 6: return QKN_HEAD_KERNEL(6);
     case 8: return QKN_HEAD_KERNEL(8);
-    case 12: return QKN_HEAD_KERNEL(12);
-    case 16: return QKN_HEAD_KERNEL(16);
+  }
+  if constexpr (max_slots(IO::kDtype, ALIGNED) == kMaxSlots) {
+    if (v == 12) return QKN_HEAD_KERNEL(12);
+    if (v == 16) return QKN_HEAD_KERNEL(16);
   }
 #undef QKN_HEAD_KERNEL
   return nullptr;

@@ -190,6 +190,23 @@ def test_widest_rows_and_beyond():
     assert e.value.status == UNSUPPORTED
 
 
+@pytest.mark.parametrize("dtype,aligned,max_chunks", [
+    ("bf16", True, 8192), ("f32", True, 8192), ("fp8", True, 4096),
+    ("bf16", False, 4096), ("f32", False, 6144), ("fp8", False, 2048)])
+def test_row_width_limit_per_path(dtype, aligned, max_chunks):
+    """Q + K chunks per shard: the widest row that plans, and one chunk more
+    that is refused as unsupported, with every kernel's slots in registers."""
+    vw = {"bf16": 8, "f32": 4, "fp8": 16}[dtype]
+    hk = 4 * vw
+    pad = 0 if aligned else 1                      # odd row stride: element-wise path
+    hq = (max_chunks - 4) * vw
+    d = qk.describe_plan(OP_FUSED, hq, hk, 100, dtype, 1, ld=hq + hk + pad)
+    assert ("path=16B" if aligned else "elementwise") in d
+    with pytest.raises(qk.QKNormError) as e:
+        qk.describe_plan(OP_FUSED, hq + vw, hk, 100, dtype, 1, ld=hq + vw + hk + pad)
+    assert e.value.status == UNSUPPORTED
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
