@@ -230,6 +230,8 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
   a.inv_divk = (float)(1.0 / (double)(mode == qkn::MODE_APPLY ? hk_full : k->h));
   a.log2_lanes = 0;
   while ((1 << a.log2_lanes) < a.lanes) ++a.log2_lanes;
+  a.log2_tok = 0;
+  while ((1 << a.log2_tok) < a.tok_threads) ++a.log2_tok;
   a.log2_group = 0;
   while ((1 << a.log2_group) < out->plan.group) ++a.log2_group;
   a.groups_per_shard = out->plan.lanes / out->plan.group;
@@ -387,8 +389,9 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   r.nck = (int)nck;
   const int nc = r.ncq + r.nck;
 
-  // Candidate lane counts per shard: powers of two below 64 (several shards
-  // share a wave) and multiples of 64 (a shard spans whole waves).
+  // Candidate lane counts per shard: powers of two below 64 (several shards,
+  // or several tokens, share a wave) and multiples of 64 (a shard spans whole
+  // waves).
   struct Cand {
     int lanes, slots;
     int64_t waste;
@@ -397,9 +400,12 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   double best_score = 1e30;
   const bool few_tokens = T < 1024;  // under ~4 tokens per CU: favour latency
   // Slots per lane for `l` lanes per shard, or 0 if that layout does not fit a block.
+  // Several tokens share a wave only without shards and with enough tokens
+  // to fill the waves.
+  const bool sub_wave = shards == 1 && !few_tokens;
   auto fits_block = [&](int l) {
     const int g = shards * l;
-    if (g % 64 || g > kMaxThreads) return 0;
+    if (g > kMaxThreads || (g % 64 && !(sub_wave && g < 64))) return 0;
     const int v = slots_for(ceil_div(nc, l), max_slots(dtype, aligned));
     return (v && g <= max_threads_for_slots(v, dtype, aligned)) ? v : 0;
   };
@@ -429,9 +435,10 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   r.slots = best.slots;
   r.group = best.lanes < 64 ? best.lanes : 64;
   r.tok_threads = shards * best.lanes;
-  r.waves = r.tok_threads / 64;
-  // One-wave tokens are packed four to a block; wider tokens get a block each.
-  r.tokens_per_block = (r.waves == 1 && !few_tokens) ? 4 : 1;
+  r.waves = (r.tok_threads + 63) / 64;
+  // Tokens of one wave or less are packed four waves to a block; wider tokens
+  // get a block each.
+  r.tokens_per_block = r.tok_threads < 64 ? 4 * 64 / r.tok_threads : (r.waves == 1 && !few_tokens) ? 4 : 1;
   if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots, dtype, aligned)) r.tokens_per_block = 1;
   r.threads = r.tokens_per_block * r.tok_threads;
   const int groups_per_token = r.tok_threads / r.group;

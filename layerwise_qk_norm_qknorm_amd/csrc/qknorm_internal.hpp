@@ -89,6 +89,7 @@ struct RowArgs {
   int shards;
   int lanes, group, tok_threads, tokens_per_block;
   int log2_lanes;     // log2(lanes) when shards > 1 (lanes is then a power of two)
+  int log2_tok;       // log2(tok_threads) when several tokens share a block (a power of two <= 64)
   int log2_group;     // log2(group)
   int groups_per_shard, groups_per_token;
   float inv_divq, inv_divk;  // 1/H for Q and K in Eq. 1, rounded once

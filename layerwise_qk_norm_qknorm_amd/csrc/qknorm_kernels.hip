@@ -331,11 +331,12 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
   const int L = a.lanes;
-  // Tokens share a block only when each takes one wave, and shards share a
-  // token only with power-of-two lane groups, so the lane decomposition is
-  // shifts and masks.
-  const int j = a.tokens_per_block > 1 ? tid >> 6 : 0;   // token slot within the block
-  const int r = a.tokens_per_block > 1 ? tid & 63 : tid;  // thread within the token
+  // Tokens share a block only when each takes a power-of-two share of one
+  // wave (64 lanes, or 4..32 so that several tokens share a wave), and shards
+  // share a token only with power-of-two lane groups, so the lane
+  // decomposition is shifts and masks.
+  const int j = a.tokens_per_block > 1 ? tid >> a.log2_tok : 0;   // token slot within the block
+  const int r = a.tokens_per_block > 1 ? tid & (G - 1) : tid;     // thread within the token
   const int s = a.shards > 1 ? r >> a.log2_lanes : 0;     // shard group
   const int m = a.shards > 1 ? r & (L - 1) : r;           // lane within the group
   const int qbase = __umul24(s, a.hq_s), kbase = __umul24(s, a.hk_s);
@@ -408,13 +409,17 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       // Across the lanes of a group: every lane ends with the group's sum.
       aq = group_sum(aq, group);
       ak = group_sum(ak, group);
-      if (G == 64) {
+      if (G <= 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
+        // Several tokens per wave (one shard each): the group is the token.
         if (MODE == MODE_STATS) {
           if (m == 0 && active) {
             a.partials[(int64_t)(2 * s) * a.T + t] = aq;
             a.partials[(int64_t)(2 * s + 1) * a.T + t] = ak;
           }
+        } else if (G < 64) {
+          ssq = aq;
+          ssk = ak;
         } else {
           ssq = lane_read(aq, 0);
           ssk = lane_read(ak, 0);

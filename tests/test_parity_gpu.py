@@ -288,6 +288,43 @@ def test_elementwise_path(dtype):
     _custom_case(17, 4100, 1030, 2, dtype, 2, seed=44, offset=3, ld_pad=1)
 
 
+@pytest.mark.parametrize("T,hq,hk,hv,dtype,offset", [
+    (1500, 128, 64, 64, "bf16", 0),     # 24 chunks: 8 lanes per token, 8 tokens per wave
+    (2000, 64, 32, 0, "f32", 0),        # 24 fp32 chunks: 8 lanes per token
+    (1100, 40, 24, 8, "bf16", 0),       # 8 chunks: 4 lanes per token, 16 per wave, ragged slots
+    (4097, 640, 128, 128, "bf16", 0),   # 96 chunks: 32 lanes per token, ragged last block
+    (1025, 128, 64, 0, "bf16", 1),      # element-wise path, several tokens per wave
+])
+def test_several_tokens_per_wave(T, hq, hk, hv, dtype, offset):
+    """Rows of fewer than 64 lanes' chunks: several tokens share a wave, each
+    reduced over its own lane group; token counts that leave the last block
+    partly empty."""
+    ld = hq + hk + hv
+    plan = qk.describe_plan(0, hq, hk, T, dtype, 1, ld=ld, aligned=offset == 0)
+    tok_threads = int(plan.split("threads/token=")[1].split()[0])
+    assert tok_threads < 64, plan
+    _log(f"[plan] {plan}")
+    _custom_case(T, hq, hk, hv, dtype, 1, seed=T + hq, offset=offset)
+
+
+def test_several_tokens_per_wave_fused_equals_split_bitwise():
+    inp = I.make_custom(3000, 256, 128, 0, "bf16", seed=61)
+    assert "threads/token=16" in qk.describe_plan(0, 256, 128, 3000, "bf16", 1, ld=256)
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    fq, fk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 1, fq, fk)
+    part = qk.qknorm_partial_stats(xq, xk, 1)
+    aq, ak = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, part, 256, 128, aq, ak)
+    torch.cuda.synchronize()
+    ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", 1)
+    got_p = part.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_p - ref_p) <= 1e-5 * ref_p)
+    assert torch.equal(fq.view(torch.int16), aq.view(torch.int16))
+    assert torch.equal(fk.view(torch.int16), ak.view(torch.int16))
+
+
 def test_elementwise_path_is_bitwise_identical_to_vector_path():
     """Same data through the 16-byte path and (shifted by one element) the
     element-wise path: the reduction order is the same, so are the bits."""
