@@ -240,12 +240,20 @@ __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<I
       decode<IO>(xv[i], xf);
       decode_gamma<IO>(g[i], gf);
 #pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        y[i][e] = (xf[e] * gf[e]) * r[i];
-        if (cnt[i] > 0) big = __builtin_fmaxf(big, __builtin_fabsf(y[i][e]));
-      }
+      for (int e = 0; e < VW; ++e) y[i][e] = (xf[e] * gf[e]) * r[i];
+      // Largest magnitude of the slot (NaN if any is NaN), one three-operand
+      // maximum per two elements; idle slots are left out once per slot.
+      float sm = __builtin_fabsf(y[i][0]);
+#pragma unroll
+      for (int e = 1; e + 1 < VW; e += 2)
+        sm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sm, __builtin_fabsf(y[i][e])),
+                                           __builtin_fabsf(y[i][e + 1]));
+      if (VW % 2 == 0) sm = __builtin_elementwise_maximum(sm, __builtin_fabsf(y[i][VW - 1]));
+      if (cnt[i] > 0) big = __builtin_elementwise_maximum(big, sm);
     }
-    const bool clamp = __builtin_amdgcn_ballot_w64(active && big > 448.0f) != 0;
+    // A NaN (from gamma, say) sends the wave through the saturating path too,
+    // which keeps NaN and clamps the rest.
+    const bool clamp = __builtin_amdgcn_ballot_w64(active && !(big <= 448.0f)) != 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       if (clamp) {

@@ -154,6 +154,21 @@ def test_fp8_saturates_instead_of_nan():
     _compare(out, ref, "fp8 saturation")
 
 
+def test_fp8_nan_gamma_with_overflow():
+    """A NaN gamma column next to results beyond 448: NaN stays in that
+    column, everything else saturates (the clamp decision sees the NaN)."""
+    inp = I.make_custom(64, 512, 128, 0, "fp8", seed=802)
+    g = np.full(512, 300.0)
+    g[5] = np.nan
+    inp.gamma_q[...] = I.to_bf16_bits(g)
+    out, ref = _fused(inp, 0, 1)
+    assert np.all((out[:, 5] & 0x7F) == 0x7F)
+    big = np.abs(ref.yq) > 464
+    assert big.sum() > 1000
+    assert np.all((out[:, :512][big] & 0x7F) == 0x7E)
+    _compare(out, ref, "fp8 NaN gamma")
+
+
 def test_fp8_elementwise_path():
     _compare(*_fused(I.make_custom(45, 40 * 8, 24, 0, "fp8", seed=901), 8, 1, offset=3), "fp8 misaligned")
     _compare(*_fused(I.make_custom(31, 1000, 200, 0, "fp8", seed=902), 0, 4, ld_pad=1), "fp8 odd stride")
