@@ -39,14 +39,20 @@ namespace {
 // I/O types. kVW: elements per 16-byte row chunk; kBytes: bytes per row
 // element; kGW / kGBytes: 32-bit words of gamma per chunk and bytes per gamma
 // element (FP8 rows take bf16 gamma).
+// kSwap: the 16- and 32-lane steps of the lane sums use permlane swaps (else
+// the LDS crossbar); chosen per type by measurement on MI355X (the swaps
+// were faster for bf16 rows, slower for FP8 rows).
 struct BF16 {
   static constexpr int kVW = 8, kBytes = 2, kGW = 4, kGBytes = 2, kDtype = kDtypeBF16;
+  static constexpr bool kSwap = true;
 };
 struct F32 {
   static constexpr int kVW = 4, kBytes = 4, kGW = 4, kGBytes = 4, kDtype = kDtypeF32;
+  static constexpr bool kSwap = true;
 };
 struct FP8 {  // OCP FP8 E4M3 (E4M3FN) rows, bf16 gamma
   static constexpr int kVW = 16, kBytes = 1, kGW = 8, kGBytes = 2, kDtype = kDtypeFP8;
+  static constexpr bool kSwap = false;
 };
 
 template <int W>
@@ -310,21 +316,36 @@ __device__ __forceinline__ void keep_packed(Words<W>& c) {
 // lane of a group ends with the same value. Inside a 16-lane row the steps
 // are DPP moves fused into the adds (quad permutes, then the half-row and
 // row mirrors, which pair lanes of the two halves once each half is
-// uniform); only the 16- and 32-lane steps cross rows through the LDS
-// crossbar. Each step adds two lanes' values, a + b on one and b + a on the
-// other, so all lanes of a group hold bitwise the same sum.
+// uniform). The 16- and 32-lane steps cross rows either through the LDS
+// crossbar or with gfx950's permlane swaps: swapping the odd rows (or the
+// upper half) of one copy with the even rows (lower half) of another leaves
+// row pairs (halves) side by side in the two results, so one add gives every
+// lane the pair's sum. Both give the same bits. Each step adds
+// two lanes' values, a + b on one and b + a (or a + b) on the other, so all
+// lanes of a group hold bitwise the same sum.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float swap_add16(float v) {  // lanes i ^ 16
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float swap_add32(float v) {  // lanes i ^ 32
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <bool SWAP>
 __device__ __forceinline__ float group_sum(float v, int group) {
   if (group > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
   if (group > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
   if (group > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
   if (group > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
-  if (group > 16) v += __shfl_xor(v, 16);
-  if (group > 32) v += __shfl_xor(v, 32);
+  if (group > 16) v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
+  if (group > 32) v = SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
   return v;
 }
 
@@ -353,24 +374,17 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   bool isq[V];
   int col[V];
   int cnt[V];
+  // Selects rather than branches: an idle slot (u past the last chunk) reads
+  // and ignores the first chunk of the Q row.
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int u = i * L + m;
-    if (u < a.ncq) {
-      const int c = u * VW;
-      isq[i] = true;
-      col[i] = qbase + c;
-      cnt[i] = ALIGNED ? VW : min(VW, a.hq_s - c);
-    } else if (u < a.ncq + a.nck) {
-      const int c = (u - a.ncq) * VW;
-      isq[i] = false;
-      col[i] = kbase + c;
-      cnt[i] = ALIGNED ? VW : min(VW, a.hk_s - c);
-    } else {  // idle slot: reads (and ignores) the first chunk of the Q row
-      isq[i] = true;
-      col[i] = 0;
-      cnt[i] = 0;
-    }
+    const bool q = u < a.ncq;
+    const bool idle = u >= a.ncq + a.nck;
+    const int c = (q ? u : u - a.ncq) * VW;
+    isq[i] = q || idle;
+    col[i] = idle ? 0 : (q ? qbase : kbase) + c;
+    cnt[i] = idle ? 0 : ALIGNED ? VW : min(VW, (q ? a.hq_s : a.hk_s) - c);
   }
 
   GChunk<IO> g[MODE == MODE_STATS ? 1 : V];
@@ -415,8 +429,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         ak += isq[i] ? 0.0f : cs;
       }
       // Across the lanes of a group: every lane ends with the group's sum.
-      aq = group_sum(aq, group);
-      ak = group_sum(ak, group);
+      aq = group_sum<IO::kSwap>(aq, group);
+      ak = group_sum<IO::kSwap>(ak, group);
       if (G <= 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
         // Several tokens per wave (one shard each): the group is the token.
@@ -560,7 +574,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
-    acc = group_sum(acc, L);
+    acc = group_sum<IO::kSwap>(acc, L);
 
     {
       if (IO::kBytes < 4 && V > 4) {
@@ -640,7 +654,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float ss[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
+    for (int i = 0; i < V; ++i) ss[i] = group_sum<IO::kSwap>(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
 
     {
       if (IO::kBytes < 4 && V > 4) {
