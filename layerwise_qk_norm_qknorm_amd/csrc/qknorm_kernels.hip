@@ -8,10 +8,12 @@
 //   - Phase B and the final scaling: x * gamma, then times the RMS factor;
 //     only the final result is written to memory.
 //
-// One kernel template serves the three entry points (MODE_FUSED,
-// MODE_STATS, MODE_APPLY) so that the per-shard sums are produced by the
-// same instructions in every mode, which is what makes the fused call and
-// the split calls agree bit for bit.
+// One kernel template, qknorm_rows, serves the three layerwise entry points
+// (MODE_FUSED, MODE_STATS, MODE_APPLY) so that the per-shard sums are
+// produced by the same instructions in every mode, which is what makes the
+// fused call and the split calls agree bit for bit. qknorm_heads_packed and
+// qknorm_heads serve the headwise entry point (the introduction's per-head
+// granularity) with the same load, convert, scale and store helpers.
 //
 // This is a streaming, HBM-bound operation (about 1 flop per byte): there is
 // no contraction, so no MFMA. What matters is that every Q/K element is read
@@ -21,10 +23,11 @@
 // Work layout (see Plan in qknorm_internal.hpp): G = S * L threads handle
 // one token; the L lanes of shard group s own the 16-byte chunks of Q shard
 // s followed by K shard s, lane m taking chunks m, m+L, m+2L, ... (`slots`
-// of them, about three). A block holds one or a few tokens side by side and
-// there is one block per such group of tokens, so many independent tokens
-// have their loads in flight on every CU; gamma is reloaded per block from
-// the caches (it is small and shared by all tokens).
+// of them, about three). A block holds one or a few tokens side by side
+// (narrow rows: several tokens per wave) and there is one block per such
+// group of tokens, so many independent tokens have their loads in flight on
+// every CU; gamma is reloaded per block from the caches (it is small and
+// shared by all tokens).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -230,8 +233,8 @@ __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
 // y = (x * gamma) * r[i], one rounding to the I/O type, stores of the valid
 // chunks (slot i goes to the Q or the K row). For FP8 the saturating
 // conversion costs four operations per element, so with up to 4 slots the
-// wave first checks whether any result exceeds 448 in magnitude (NaN results
-// need no clamp: they convert to NaN) and clamps only then.
+// wave first checks whether any result exceeds 448 in magnitude or is NaN,
+// and clamps only then.
 template <class IO, int V, bool ALIGNED>
 __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<IO> (&g)[V], const float (&r)[V],
                                             const bool (&isq)[V], const int (&col)[V], const int (&cnt)[V],

@@ -340,6 +340,47 @@ def test_many_shards_and_widest_rows():
     _custom_case(3, 49152, 16384, 0, "bf16", 8, seed=54)
 
 
+def test_row_offsets_beyond_4_gib():
+    """Packed bf16 rows [262147, 8192] (4.3 GB): rows past the first 4 GiB need
+    64-bit offsets. Inputs are drawn on the device from a seeded generator;
+    sampled rows are copied back and checked against the oracle one by one,
+    for the fused call and for partial_stats + apply_with_stats."""
+    T, hq, hk, ld = 262147, 4096, 1024, 8192
+    assert (T - 1) * ld * 2 > 1 << 32
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(20260)
+    x = torch.randn((T, ld), generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(20261)
+    gq_bits = I.to_bf16_bits(rng.normal(1.0, 0.1, hq))
+    gk_bits = I.to_bf16_bits(rng.normal(1.0, 0.1, hk))
+    gq, gk = np_to_torch(gq_bits).to(DEV), np_to_torch(gk_bits).to(DEV)
+    y = torch.zeros_like(x)
+    _log(f"[case] 4 GiB rows T={T} ld={ld} plan: {qk.describe_plan(0, hq, hk, T, 'bf16', 1, ld=ld)}")
+    qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], gq, gk, 1e-6, 1, y[:, :hq], y[:, hq:hq + hk])
+    part = qk.qknorm_partial_stats(x[:, :hq], x[:, hq:hq + hk], 1)
+    y2 = torch.zeros_like(x)
+    qk.qknorm_apply_with_stats(x[:, :hq], x[:, hq:hq + hk], gq, gk, 1e-6, part, hq, hk, y2[:, :hq], y2[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, T // 2, 262143, 262144, T - 2, T - 1],
+                                     rng.integers(0, T, 25)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    xs = torch_to_np(x.index_select(0, idx))
+    ys = torch_to_np(y.index_select(0, idx))
+    ys2 = torch_to_np(y2.index_select(0, idx))
+    ps = part.index_select(2, idx).cpu().numpy().astype(np.float64)
+    del x, y, y2
+    torch.cuda.empty_cache()
+    ref = oracle.qknorm_fused(xs[:, :hq], xs[:, hq:hq + hk], gq_bits, gk_bits, "bf16", 1e-6, 1)
+    check_bf16(ys[:, :hq], ref.yq_bits, "4 GiB Q")
+    check_bf16(ys[:, hq:hq + hk], ref.yk_bits, "4 GiB K")
+    assert not ys[:, hq + hk:].any(), "V columns were written"
+    assert np.array_equal(ys, ys2), "split path differs from fused"
+    ref_p = oracle.qknorm_partial_stats(xs[:, :hq], xs[:, hq:hq + hk], "bf16", 1)
+    assert np.all(np.abs(ps - ref_p) <= 1e-5 * ref_p)
+    _log(f"[parity] 4 GiB rows: {len(rows)} sampled rows match")
+
+
 def test_too_wide_is_unsupported_and_writes_nothing():
     T, hq, hk = 2, 65536, 8
     x = torch.zeros((T, hq + hk), dtype=torch.bfloat16, device=DEV)
