@@ -60,10 +60,12 @@
  * ------
  * Argument errors return QKNORM_ERR_INVALID_ARG before anything is launched
  * and nothing is written; QKNORM_ERR_UNSUPPORTED means valid arguments that
- * this library cannot run (a row wider than the kernels hold: per shard, Q
- * plus K columns of up to 8192 16-byte chunks for bf16 and fp32 and 4096 for
- * FP8, i.e. 65536 bf16 / 32768 fp32 / 65536 FP8 elements, on the 16-byte
- * path; about 4096 / 6144 / 2048 chunks on the element-wise path);
+ * this library cannot run (a row wider than the kernels hold). With one
+ * shard a token's Q plus K columns may span up to 8192 16-byte chunks for
+ * bf16 and fp32 and 4096 for FP8 (65536 bf16 / 32768 fp32 / 65536 FP8
+ * elements) on the 16-byte path, and about 4096 / 6144 / 2048 chunks on the
+ * element-wise path. With S > 1 shards each shard takes a power-of-two lane
+ * group of at most 1024/S lanes, so a shard holds proportionally fewer.
  * QKNORM_ERR_HIP
  * means a HIP runtime call failed. qknorm_last_error() gives the message.
  * Faults inside kernels surface at the caller's next synchronization. T == 0

@@ -1,0 +1,139 @@
+"""Property tests of the host planners (CPU only, no kernel runs): for many
+shapes, every launch the library would make fits the kernel it picks (slot
+counts that exist, block sizes within that kernel's register budget, lane
+groups that cover every chunk, LDS sized for the block), and a shape is
+refused as unsupported only when no layout of the kernel family holds it."""
+
+import re
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import layerwise_qk_norm_qknorm_amd as qk
+
+SLOTS = (1, 2, 3, 4, 6, 8, 12, 16)
+VW = {"bf16": 8, "f32": 4, "fp8": 16}
+UNSUPPORTED = 2
+
+
+def max_threads(v, dtype, aligned):
+    lim = (3 if dtype == "fp8" else 8) if aligned else {"f32": 6, "bf16": 4, "fp8": 1}[dtype]
+    return 1024 if v <= lim else 256
+
+
+def max_slots(dtype, aligned):
+    return 8 if (dtype == "fp8" and not aligned) else 16
+
+
+def slots_for(n, dtype, aligned):
+    for s in SLOTS:
+        if s >= n:
+            return s if s <= max_slots(dtype, aligned) else 0
+    return 0
+
+
+def fields(desc):
+    return {k: v for k, v in re.findall(r"([a-z_/]+)=(\S+)", desc)}
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def feasible_layerwise(nc, shards, T, dtype, aligned):
+    sub_wave = shards == 1 and T >= 1024
+    ls = [4, 8, 16, 32] + list(range(64, 1025, 64))
+    for l in ls:
+        if shards > 1 and (l & (l - 1)):
+            continue
+        g = shards * l
+        if g > 1024 or (g % 64 and not (sub_wave and g < 64)):
+            continue
+        v = slots_for(ceil_div(nc, l), dtype, aligned)
+        if v and g <= max_threads(v, dtype, aligned):
+            return True
+    return False
+
+
+@settings(max_examples=400, deadline=None, derandomize=True)
+@given(dtype=st.sampled_from(["bf16", "f32", "fp8"]), shards=st.sampled_from([1, 1, 2, 3, 4, 8, 16, 64]),
+       hq_s=st.integers(1, 9000), hk_s=st.integers(1, 3000), T=st.sampled_from([1, 7, 100, 1023, 1024, 5000, 100000]),
+       op=st.sampled_from([0, 1, 2]), unaligned=st.booleans())
+def test_layerwise_plans_fit_their_kernels(dtype, shards, hq_s, hk_s, T, op, unaligned):
+    vw = VW[dtype]
+    if not unaligned:  # whole 16-byte chunks per shard: the 16-byte path
+        hq_s, hk_s = ceil_div(hq_s, vw) * vw, ceil_div(hk_s, vw) * vw
+    hq, hk = hq_s * shards, hk_s * shards
+    ld = hq + hk + (1 if unaligned else 0)
+    if op == 2:  # apply_with_stats takes combined statistics: one shard over the local width
+        shards, hq_s, hk_s = 1, hq, hk
+    nc = ceil_div(hq_s, vw) + ceil_div(hk_s, vw)
+    try:
+        d = qk.describe_plan(op, hq, hk, T, dtype, shards, ld=ld)
+    except qk.QKNormError as e:
+        assert e.status == UNSUPPORTED
+        aligned = not unaligned
+        assert not feasible_layerwise(nc, shards, T, dtype, aligned), "a feasible shape was refused"
+        return
+    f = fields(d)
+    aligned = f["path"] == "16B"
+    assert aligned == (not unaligned)
+    lanes, slots = int(f["lanes/shard"]), int(f["slots"])
+    G, tpb, lds = int(f["threads/token"]), int(f["tokens/block"]), int(f["lds"])
+    assert f["chunks"] == f"({ceil_div(hq_s, vw)},{ceil_div(hk_s, vw)})"
+    assert slots in SLOTS and slots <= max_slots(dtype, aligned)
+    assert lanes * slots >= nc                       # every chunk has a lane slot
+    assert G == shards * lanes
+    if shards > 1:
+        assert lanes & (lanes - 1) == 0
+    if G % 64:                                       # several tokens per wave
+        assert G < 64 and 64 % G == 0 and shards == 1 and T >= 1024
+    assert tpb >= 1 and (tpb == 1 or G <= 64)
+    assert tpb * G <= max_threads(slots, dtype, aligned)
+    waves = ceil_div(G, 64)
+    group = min(lanes, 64)
+    assert lds == (2 * tpb * (G // group) * 2 * 4 if waves > 1 else 0)
+    assert lds <= 64 * 1024
+
+
+def feasible_headwise(heads, nc, dtype, aligned):
+    if nc > 64 * 8 or heads * 4 > 1024:
+        return False
+    l = 4
+    while l <= 64:
+        v = slots_for(ceil_div(nc, l), dtype, aligned)
+        if v and ceil_div(heads * l, 64) * 64 <= max_threads(v, dtype, aligned):
+            return True
+        l *= 2
+    return False
+
+
+@settings(max_examples=300, deadline=None, derandomize=True)
+@given(dtype=st.sampled_from(["bf16", "f32", "fp8"]), head_dim=st.sampled_from([8, 16, 36, 64, 72, 96, 128, 256,
+                                                                               512, 2048, 4096]),
+       hq_heads=st.integers(1, 128), hk_heads=st.integers(1, 32), T=st.sampled_from([1, 50, 1023, 4096]),
+       stride0=st.booleans())
+def test_headwise_plans_fit_their_kernels(dtype, head_dim, hq_heads, hk_heads, T, stride0):
+    hq, hk = hq_heads * head_dim, hk_heads * head_dim
+    vw = VW[dtype]
+    nc = ceil_div(head_dim, vw)
+    heads = hq_heads + hk_heads
+    try:
+        d = qk.describe_headwise_plan(hq, hk, T, head_dim, dtype, 0 if stride0 else head_dim)
+    except qk.QKNormError as e:
+        assert e.status == UNSUPPORTED
+        aligned = head_dim % vw == 0
+        assert not feasible_headwise(heads, nc, dtype, aligned), "a feasible headwise shape was refused"
+        return
+    f = fields(d)
+    aligned = f["path"] == "16B"
+    slots, G, tpb, threads = int(f["slots"]), int(f["threads/token"]), int(f["tokens/block"]), int(f["threads/block"])
+    assert f["heads"] == f"({hq_heads},{hk_heads})" and int(f["chunks/head"]) == nc
+    assert slots in SLOTS and slots <= max_slots(dtype, aligned)
+    assert threads % 64 == 0 and threads >= tpb * G and threads <= max_threads(slots, dtype, aligned)
+    if f["layout"] == "token-wide":
+        assert nc & (nc - 1) == 0 and nc <= 64 and G % 64 == 0
+        assert G * slots >= heads * nc
+    else:
+        lanes = int(f["lanes/head"])
+        assert lanes & (lanes - 1) == 0 and lanes * slots >= nc and G == heads * lanes
