@@ -228,13 +228,21 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
             if el >= min_seconds or el >= max_seconds:
                 break
     el = time.perf_counter() - t0
+    # the same work on one thread, over as many chunks as fit in about 2 s
+    t1, tokens1, i = time.perf_counter(), 0, 0
+    while time.perf_counter() - t1 < 2.0 and i < 4 * len(spans):
+        tokens1 += work(spans[i % len(spans)])
+        i += 1
+    el1 = time.perf_counter() - t1
     return {
         "value": tokens / el,
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
+        "value_1_thread": tokens1 / el1,
         "sample": f"{w.key}: all {w.T} tokens x {passes} passes ({tokens} tokens, {el:.1f} s), "
-                  f"float64 NumPy oracle incl. bf16 decode and rounding, {chunk}-token chunks on {cores} threads",
+                  f"float64 NumPy oracle incl. {w.dtype} decode and rounding, {chunk}-token chunks on {cores} "
+                  f"threads; value_1_thread: {tokens1} tokens on one thread ({el1:.1f} s)",
     }
 
 
