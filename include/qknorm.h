@@ -70,8 +70,11 @@
  * means a HIP runtime call failed. qknorm_last_error() gives the message.
  * Faults inside kernels surface at the caller's next synchronization. T == 0
  * is a no-op that returns QKNORM_OK after the scalar arguments are checked.
- * Unaligned pointers or strides, or shard widths that are not a multiple of
- * 16 bytes of elements, are not errors: they run a slower element-wise path
+ * Pointers must be aligned to their element size (bf16 and bf16 gamma: 2
+ * bytes; fp32, fp32 gamma and the float32 statistics: 4 bytes); a
+ * misaligned element pointer is an argument error. Pointers or strides that
+ * are not 16-byte multiples, or shard widths that are not a multiple of 16
+ * bytes of elements, are not errors: they run a slower element-wise path
  * with bit-identical results.
  */
 #ifndef QKNORM_H

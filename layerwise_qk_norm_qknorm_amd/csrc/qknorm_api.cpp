@@ -149,11 +149,17 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
     if (!o->x) return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->x is NULL", fn, nm[c]);
     if (mode != qkn::MODE_STATS && (!o->y || !o->gamma))
       return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->y and %s->gamma are required", fn, nm[c], nm[c]);
+    if ((uintptr_t)o->x % esz ||
+        (mode != qkn::MODE_STATS && ((uintptr_t)o->y % esz || (uintptr_t)o->gamma % gamma_size(dtype))))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s pointers must be aligned to their element size", fn, nm[c]);
     if (!fits(T, o->ld_x, o->h, esz) || (mode != qkn::MODE_STATS && !fits(T, o->ld_y, o->h, esz)))
       return fail(QKNORM_ERR_INVALID_ARG, "%s: %s rows exceed the address range", fn, nm[c]);
   }
   if (mode != qkn::MODE_FUSED && !stat_buf)
     return fail(QKNORM_ERR_INVALID_ARG, "%s: %s buffer is NULL", fn, mode == qkn::MODE_STATS ? "partials" : "stats");
+  if (mode != qkn::MODE_FUSED && (uintptr_t)stat_buf % sizeof(float))
+    return fail(QKNORM_ERR_INVALID_ARG, "%s: %s buffer must be 4-byte aligned", fn,
+                mode == qkn::MODE_STATS ? "partials" : "stats");
   if (mode == qkn::MODE_STATS && T > INT64_MAX / (8 * (int64_t)shards))
     return fail(QKNORM_ERR_INVALID_ARG, "%s: partials size overflows", fn);
 
@@ -280,6 +286,8 @@ int check_and_plan_heads(const qknorm_operand_t* q, const qknorm_operand_t* k, i
   for (int c = 0; c < 2; ++c) {
     const qknorm_operand_t* o = ops[c];
     if (!o->x || !o->y || !o->gamma) return fail(QKNORM_ERR_INVALID_ARG, "%s: %s->x, y and gamma are required", fn, nm[c]);
+    if ((uintptr_t)o->x % esz || (uintptr_t)o->y % esz || (uintptr_t)o->gamma % gamma_size(dtype))
+      return fail(QKNORM_ERR_INVALID_ARG, "%s: %s pointers must be aligned to their element size", fn, nm[c]);
     if (!fits(T, o->ld_x, o->h, esz) || !fits(T, o->ld_y, o->h, esz))
       return fail(QKNORM_ERR_INVALID_ARG, "%s: %s rows exceed the address range", fn, nm[c]);
   }

@@ -90,7 +90,8 @@ def test_noop_when_T_is_zero():
 @pytest.mark.parametrize("case", [
     "null_q", "bad_dtype", "neg_T", "shards0", "shards_big", "shards_indivisible", "eps_neg", "eps_nan",
     "eps_inf", "h0", "ld_small", "ldy_small", "null_x", "null_y", "null_gamma", "yq_overlaps_yk",
-    "yq_overlaps_xk", "partial_inplace_shift", "gamma_in_output", "huge_T",
+    "yq_overlaps_xk", "partial_inplace_shift", "gamma_in_output", "huge_T", "x_misaligned", "y_misaligned",
+    "gamma_misaligned",
 ])
 def test_fused_rejects(case):
     q, k = ops()
@@ -137,6 +138,12 @@ def test_fused_rejects(case):
         q.gamma = q.y + 10 * (q.ld_y * 2)
     elif case == "huge_T":
         kw["T"] = 1 << 62
+    elif case == "x_misaligned":          # a bf16 pointer at an odd address
+        q.x = q.x + 1
+    elif case == "y_misaligned":
+        k.y = k.y + 1
+    elif case == "gamma_misaligned":
+        k.gamma = k.gamma + 1
     assert fused(q, k, **kw) == INVALID, case
     assert last_error().startswith("qknorm_fused:"), last_error()
 
@@ -160,6 +167,8 @@ def test_partial_and_apply_reject():
     assert apply(q, k, buf=0) == INVALID
     assert apply(q, k, buf=q.y) == INVALID                    # stats over the output
     assert apply(q, k, eps=-1.0) == INVALID
+    assert partial(q, k, buf=STATS + 2) == INVALID            # float32 partials must be 4-byte aligned
+    assert apply(q, k, buf=STATS + 1) == INVALID
 
 
 def test_describe_plans_of_the_workloads():
@@ -235,6 +244,9 @@ def test_headwise_rejects():
     q3, k3 = ops(hq=256, hk=128)
     q3.gamma = q3.y                                         # gamma inside an output
     assert headwise(q3, k3) == INVALID
+    q4, k4 = ops(hq=256, hk=128)
+    k4.x = k4.x + 1                                         # a bf16 input at an odd address
+    assert headwise(q4, k4) == INVALID
     assert last_error().startswith("qknorm_headwise:")
 
 
