@@ -767,9 +767,13 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   // any remainder beyond the largest grid.
   const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
   const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), (size_t)p.lds_bytes,
-                     static_cast<hipStream_t>(stream), args);
-  const hipError_t e = hipGetLastError();
+  // hipLaunchKernel returns this launch's own status (no sticky error from
+  // an earlier, unrelated call is reported as ours).
+  RowArgs a = args;
+  void* kargs[] = {&a};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
+                                       dim3((unsigned)p.threads), kargs, (size_t)p.lds_bytes,
+                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     *err = std::string("kernel launch: ") + hipGetErrorString(e);
     return (int)e;
@@ -789,8 +793,10 @@ int launch_heads(const Plan& p, const HeadArgs& args, void* stream, std::string*
   }
   const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
   const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)p.threads), 0, static_cast<hipStream_t>(stream), args);
-  const hipError_t e = hipGetLastError();
+  HeadArgs a = args;
+  void* kargs[] = {&a};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
+                                       dim3((unsigned)p.threads), kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     *err = std::string("kernel launch: ") + hipGetErrorString(e);
     return (int)e;
