@@ -229,6 +229,18 @@ __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
   return s;
 }
 
+// Largest magnitude of N values (NaN if any is NaN): one three-operand
+// maximum per two elements.
+template <int N>
+__device__ __forceinline__ float max_abs(const float (&v)[N]) {
+  float m = __builtin_fabsf(v[0]);
+#pragma unroll
+  for (int e = 1; e + 1 < N; e += 2)
+    m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(v[e])), __builtin_fabsf(v[e + 1]));
+  if (N % 2 == 0) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[N - 1]));
+  return m;
+}
+
 // Phase B and the final scaling for this lane's chunks of one token:
 // y = (x * gamma) * r[i], one rounding to the I/O type, stores of the valid
 // chunks (slot i goes to the Q or the K row). For FP8 the saturating
@@ -250,15 +262,7 @@ __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<I
       decode_gamma<IO>(g[i], gf);
 #pragma unroll
       for (int e = 0; e < VW; ++e) y[i][e] = (xf[e] * gf[e]) * r[i];
-      // Largest magnitude of the slot (NaN if any is NaN), one three-operand
-      // maximum per two elements; idle slots are left out once per slot.
-      float sm = __builtin_fabsf(y[i][0]);
-#pragma unroll
-      for (int e = 1; e + 1 < VW; e += 2)
-        sm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sm, __builtin_fabsf(y[i][e])),
-                                           __builtin_fabsf(y[i][e + 1]));
-      if (VW % 2 == 0) sm = __builtin_elementwise_maximum(sm, __builtin_fabsf(y[i][VW - 1]));
-      if (cnt[i] > 0) big = __builtin_elementwise_maximum(big, sm);
+      if (cnt[i] > 0) big = __builtin_elementwise_maximum(big, max_abs(y[i]));  // idle slots left out
     }
     // A NaN (from gamma, say) sends the wave through the saturating path too,
     // which keeps NaN and clamps the rest.
