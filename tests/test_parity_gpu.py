@@ -381,6 +381,29 @@ def test_row_offsets_beyond_4_gib():
     _log(f"[parity] 4 GiB rows: {len(rows)} sampled rows match")
 
 
+@pytest.mark.parametrize("dtype,n_planes", [("bf16", 64), ("f32", 64), ("bf16", 1), ("f32", 7)])
+def test_apply_with_many_planes(dtype, n_planes):
+    """apply_with_stats with up to the maximum number of statistic planes (one
+    per rank of a 64-way split): the planes are added in order in fp32 and
+    divided by the full widths; the oracle adds them in fp64."""
+    T, hq, hk = 300, 256, 64
+    inp = I.make_custom(T, hq, hk, 0, dtype, seed=90 + n_planes)
+    rng = np.random.default_rng(91 + n_planes)
+    local = oracle.qknorm_partial_stats(inp.q, inp.k, dtype, 1)[0]
+    # peers: sums of squares of the same scale as the local slice
+    planes = np.concatenate([local[None], local[None] * rng.uniform(0.5, 1.5, (n_planes - 1, 2, T))])
+    planes = planes.astype(np.float32)
+    hq_full, hk_full = hq * n_planes, hk * n_planes
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    yq, yk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, torch.from_numpy(planes).to(DEV), hq_full, hk_full, yq, yk)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, dtype, 1e-6, planes,
+                                         hq_full, hk_full)
+    _compare(inp.workload, torch_to_np(yq), torch_to_np(yk), ref, f"apply {n_planes} planes")
+
+
 def test_too_wide_is_unsupported_and_writes_nothing():
     T, hq, hk = 2, 65536, 8
     x = torch.zeros((T, hq + hk), dtype=torch.bfloat16, device=DEV)
