@@ -410,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_prefill")
     ap.add_argument("--shards", type=int, default=None, help="S for the fused workloads (default: first listed)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count T (a size sweep; the default is the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain copy of this many bytes instead (calibration)")
@@ -458,8 +460,13 @@ def main():
         return
 
     w = I.WORKLOADS[args.workload]
+    t_own = w.T
+    title = w.title
+    if args.tokens and args.tokens != w.T:
+        w = w.with_T(args.tokens)
+        title = f"{w.title}; T overridden to {w.T}"
     shards = args.shards or w.shards[0]
-    log(f"[bench] workload {w.key}: {w.title}")
+    log(f"[bench] workload {w.key}: {title}")
     t0 = time.perf_counter()
     inp = I.make_inputs(w)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
@@ -483,7 +490,7 @@ def main():
         f"{mean_launch_s * 1e6:.2f} us per step, {achieved:.0f} GB/s")
 
     khash = kernel_source_hash()
-    traffic = load_traffic(w.key, khash)
+    traffic = load_traffic(w.key, khash) if w.T == t_own else None  # counters were taken at the workload's T
     out = {
         "metric": "QK-Norm tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
         "value": w.T * args.steps / wall,
@@ -498,7 +505,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; inputs resident in HBM, rotating buffer sets > 1 GiB)",
         "config": {
-            "workload": w.title,
+            "workload": title,
             "key": w.key,
             "tokens": w.T,
             "hq": w.hq, "hk": w.hk, "hv": w.hv,

@@ -64,6 +64,8 @@ def library_path():
 def load_library():
     """Loads libqknorm.so once; raises if it has not been built."""
     global _lib
+    if _lib is not None:   # loaded: no lock needed to read the reference
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -101,49 +103,63 @@ def _check(rc):
 
 
 # --------------------------------------------------------------------- marshalling
+_torch = None
+_CODES = {}
+
+
+def _torch_mod():
+    global _torch
+    if _torch is None:
+        import torch
+        _CODES.update({torch.bfloat16: QKNORM_BF16, torch.float32: QKNORM_F32,
+                       torch.float8_e4m3fn: QKNORM_FP8_E4M3})
+        _torch = torch
+    return _torch
+
+
 def _dtype_code(t):
-    import torch
-    if t.dtype == torch.bfloat16:
-        return QKNORM_BF16
-    if t.dtype == torch.float32:
-        return QKNORM_F32
-    if t.dtype == torch.float8_e4m3fn:
-        return QKNORM_FP8_E4M3
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float32 or float8_e4m3fn)")
+    _torch_mod()
+    code = _CODES.get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float32 or float8_e4m3fn)")
+    return code
 
 
 def _gamma_dtype(x):
     """gamma is bf16 for FP8 rows, the row dtype otherwise."""
-    import torch
+    torch = _torch_mod()
     return torch.bfloat16 if x.dtype == torch.float8_e4m3fn else x.dtype
 
 
 def _rows(t, name):
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be 2-D [T, h], got {tuple(t.shape)}")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    shape, st = t.shape, t.stride()
+    if len(shape) != 2:
+        raise ValueError(f"{name} must be 2-D [T, h], got {tuple(shape)}")
+    if shape[1] > 1 and st[1] != 1:
         raise ValueError(f"{name} columns must be contiguous (stride(1) == 1)")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     # one-row (or empty) views can carry any stride(0); the row length is a valid ld
-    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+    return st[0] if shape[0] > 1 else max(st[0], shape[1])
 
 
 def _operand(x, y, gamma, name):
     op = Operand()
-    op.x = x.data_ptr()
     op.ld_x = _rows(x, name)
-    op.h = x.shape[1]
+    shape = x.shape
+    op.x = x.data_ptr()
+    op.h = shape[1]
     if y is not None:
-        if y.shape != x.shape:
-            raise ValueError(f"output for {name} has shape {tuple(y.shape)}, expected {tuple(x.shape)}")
-        op.y = y.data_ptr()
-        op.ld_y = _rows(y, f"out_{name}")
+        if y.shape != shape:
+            raise ValueError(f"output for {name} has shape {tuple(y.shape)}, expected {tuple(shape)}")
+        op.ld_y = _rows(y, "output for " + name)
         if y.dtype != x.dtype:
             raise TypeError(f"output for {name} must have dtype {x.dtype}")
+        op.y = y.data_ptr()
     if gamma is not None:
-        if gamma.dim() != 1 or gamma.shape[0] != x.shape[1] or (gamma.shape[0] > 1 and gamma.stride(0) != 1):
-            raise ValueError(f"gamma for {name} must be contiguous [{x.shape[1]}]")
+        gs = gamma.shape
+        if len(gs) != 1 or gs[0] != shape[1] or (gs[0] > 1 and gamma.stride(0) != 1):
+            raise ValueError(f"gamma for {name} must be contiguous [{shape[1]}]")
         if gamma.dtype != _gamma_dtype(x):
             raise TypeError(f"gamma for {name} must have dtype {_gamma_dtype(x)}")
         op.gamma = gamma.data_ptr()
@@ -151,12 +167,12 @@ def _operand(x, y, gamma, name):
 
 
 def _stream(t, stream):
-    import torch
+    torch = _torch_mod()
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
     if raw is not None:   # the current stream's handle without building a Stream object
-        return raw(t.device.index if t.device.index is not None else torch.cuda.current_device())
+        return raw(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -165,7 +181,7 @@ def _tokens(q, k):
         raise ValueError(f"q has {q.shape[0]} rows, k has {k.shape[0]}")
     if q.dtype != k.dtype:
         raise TypeError("q and k must have the same dtype")
-    if q.device != k.device:
+    if q.get_device() != k.get_device():
         raise ValueError("q and k must be on the same device")
     return q.shape[0]
 
