@@ -407,7 +407,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # Warm-up long enough (tens of ms at the prefill shapes) for clocks and
+    # the rotating buffers' first touches to settle before timing.
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="gqa_prefill")
     ap.add_argument("--shards", type=int, default=None, help="S for the fused workloads (default: first listed)")
     ap.add_argument("--tokens", type=int, default=None,
