@@ -53,8 +53,12 @@
  * ---------------------
  * The caller owns every buffer. The library allocates nothing and keeps no
  * state except a per-thread error message. Work is enqueued on `stream` (a
- * hipStream_t; NULL means the default stream) and the call returns without
- * synchronizing. All pointers are device pointers.
+ * hipStream_t; NULL means the default stream of the calling thread's current
+ * device) and the call returns without synchronizing. The kernel runs on the
+ * stream's device; all pointers are device pointers that this device can
+ * access. Calls on different streams or threads are independent; two calls
+ * whose outputs overlap race, as any two kernels would. The kernels are
+ * built for gfx950 only.
  *
  * Errors
  * ------
