@@ -182,3 +182,67 @@ def test_fp8_nan_rows():
     out, ref = _fused(inp, 0, 1)
     assert np.all((out[3, :256] & 0x7F) == 0x7F) and np.all((out[5, 256:320] & 0x7F) == 0x7F)
     _compare(out, ref, "fp8 NaN rows")
+
+
+def test_fp8_in_place_equals_out_of_place():
+    inp = I.make_custom(200, 1024, 256, 0, "fp8", seed=1101)
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    oq, ok = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 2, oq, ok)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 2)          # in place
+    torch.cuda.synchronize()
+    assert torch.equal(xq.view(torch.uint8), oq.view(torch.uint8))
+    assert torch.equal(xk.view(torch.uint8), ok.view(torch.uint8))
+
+
+def test_fp8_many_shards_split_equals_fused():
+    inp = I.make_custom(1100, 2048, 512, 0, "fp8", seed=1102)   # 1100 tokens: ragged last block
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    fq, fk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 8, fq, fk)
+    part = qk.qknorm_partial_stats(xq, xk, 8)
+    aq, ak = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, part, 2048, 512, aq, ak)
+    torch.cuda.synchronize()
+    assert torch.equal(fq.view(torch.uint8), aq.view(torch.uint8))
+    assert torch.equal(fk.view(torch.uint8), ak.view(torch.uint8))
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", 1e-6, 8)
+    check_fp8(torch_to_np(fq), ref.yq_bits, "S=8 Q")
+    check_fp8(torch_to_np(fk), ref.yk_bits, "S=8 K")
+    ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "fp8", 8)
+    got_p = part.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_p - ref_p) <= 1e-5 * ref_p)
+
+
+def test_fp8_subnormal_inputs_and_results():
+    """E4M3 subnormals (multiples of 2^-9) in, results down to the subnormal
+    range out (a small gamma)."""
+    inp = I.make_custom(64, 512, 128, 0, "fp8", seed=1103)
+    rng = np.random.default_rng(1104)
+    inp.q[:, ::3] = rng.integers(1, 8, inp.q[:, ::3].shape).astype(np.uint8)        # +subnormals
+    inp.k[:, 1::4] = (rng.integers(1, 8, inp.k[:, 1::4].shape) | 0x80).astype(np.uint8)  # -subnormals
+    inp.gamma_q[...] = I.to_bf16_bits(np.full(512, 2.0 ** -8))
+    out, ref = _fused(inp, 0, 1)
+    sub = (ref.yq_bits & 0x78) == 0
+    assert sub.sum() > 100                      # many results are E4M3 subnormals
+    _compare(out, ref, "fp8 subnormals")
+
+
+@pytest.mark.parametrize("head_dim,stride", [(64, 0), (64, 64), (80, 0), (72, 72)])
+def test_fp8_headwise_head_sizes(head_dim, stride):
+    heads_q, heads_k = 12, 4
+    hq, hk = heads_q * head_dim, heads_k * head_dim
+    inp = I.make_custom(77, hq, hk, 0, "fp8", seed=1200 + head_dim + stride)
+    gq_h = inp.gamma_q[:head_dim].copy() if stride == 0 else inp.gamma_q
+    gk_h = inp.gamma_k[:head_dim].copy() if stride == 0 else inp.gamma_k
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    oq, ok = torch.empty_like(xq), torch.empty_like(xk)
+    _log(f"[case] fp8 headwise head_dim={head_dim} stride={stride} plan: "
+         f"{qk.describe_headwise_plan(hq, hk, 77, head_dim, 'fp8', stride)}")
+    qk.qknorm_headwise(xq, xk, np_to_torch(gq_h).to(DEV), np_to_torch(gk_h).to(DEV), 1e-6, head_dim, stride, oq, ok)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_headwise(inp.q, inp.k, gq_h, gk_h, "fp8", 1e-6, head_dim, stride)
+    check_fp8(torch_to_np(oq), ref.yq_bits, "headwise fp8 Q")
+    check_fp8(torch_to_np(ok), ref.yk_bits, "headwise fp8 K")
