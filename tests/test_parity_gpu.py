@@ -404,6 +404,41 @@ def test_apply_with_many_planes(dtype, n_planes):
     _compare(inp.workload, torch_to_np(yq), torch_to_np(yk), ref, f"apply {n_planes} planes")
 
 
+@pytest.mark.parametrize("ranks", [2, 4])
+def test_tensor_parallel_emulation_on_one_gpu(ranks):
+    """The sharded path of the paper's Phase A / Phase B, each rank's share as
+    its own calls: every rank runs partial_stats on its column slice, the
+    planes are exchanged (here: stacked in rank order), and every rank runs
+    apply_with_stats with all planes and the full widths. The slices together
+    must equal the full-row oracle, and the split must match fused(S = ranks),
+    whose per-shard sums are what the ranks would exchange."""
+    T, hq, hk = 700, 5120, 1024
+    inp = I.make_custom(T, hq, hk, 0, "bf16", seed=3000 + ranks)
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    wq, wk = hq // ranks, hk // ranks
+    planes = torch.cat([qk.qknorm_partial_stats(xq[:, r * wq:(r + 1) * wq], xk[:, r * wk:(r + 1) * wk], 1)
+                        for r in range(ranks)])                       # [ranks, 2, T], rank order
+    yq, yk = torch.empty_like(xq), torch.empty_like(xk)
+    for r in range(ranks):
+        qk.qknorm_apply_with_stats(xq[:, r * wq:(r + 1) * wq], xk[:, r * wk:(r + 1) * wk], gq[r * wq:(r + 1) * wq],
+                                   gk[r * wk:(r + 1) * wk], 1e-6, planes, hq, hk,
+                                   yq[:, r * wq:(r + 1) * wq], yk[:, r * wk:(r + 1) * wk])
+    fq, fk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, 1e-6, ranks, fq, fk)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "bf16", 1e-6, 1)
+    check_bf16(torch_to_np(yq), ref.yq_bits, f"{ranks} ranks Q")
+    check_bf16(torch_to_np(yk), ref.yk_bits, f"{ranks} ranks K")
+    # the ranks' planes are the fused kernel's per-shard sums up to summation order
+    ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", ranks)
+    got_p = planes.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_p - ref_p) <= 1e-5 * ref_p)
+    fq_np, yq_np = torch_to_np(fq), torch_to_np(yq)
+    assert np.mean(fq_np == yq_np) > 0.99     # same math, same rounding almost everywhere
+    _log(f"[parity] tensor-parallel emulation, {ranks} ranks: slices match the full-row oracle")
+
+
 def test_too_wide_is_unsupported_and_writes_nothing():
     T, hq, hk = 2, 65536, 8
     x = torch.zeros((T, hq + hk), dtype=torch.bfloat16, device=DEV)
