@@ -60,20 +60,25 @@ def to_device(a, dev):
 
 # ----------------------------------------------------------------------------- steps
 class FusedStep:
-    """One qknorm_fused call over a packed QKV buffer set."""
+    """One qknorm_fused (or qknorm_headwise) call over a buffer set: packed
+    QKV rows, or separate Q and K arrays for the workloads laid out that way."""
 
     def __init__(self, w, inp, dev, shards):
         import torch
         import layerwise_qk_norm_qknorm_amd as qk
         self.qk, self.w, self.shards = qk, w, shards
-        x0 = to_device(inp.qkv, dev)
-        per_set = 2 * x0.numel() * x0.element_size()
+        if w.packed:
+            x0 = to_device(inp.qkv, dev)
+            srcs = [x0]
+        else:
+            srcs = [to_device(inp.q, dev), to_device(inp.k, dev)]
+            x0 = srcs[0]
+        per_set = 2 * sum(t.numel() * t.element_size() for t in srcs)
         self.n_sets = max(1, -(-ROTATE_MIN_BYTES // per_set))
         self.sets = []
         for i in range(self.n_sets):
-            x = x0 if i == 0 else x0.clone()
-            y = torch.zeros_like(x0)
-            self.sets.append((x, y))
+            xs = srcs if i == 0 else [t.clone() for t in srcs]
+            self.sets.append((xs, [torch.zeros_like(t) for t in srcs]))
         esz = x0.element_size()
         gsz = inp.gamma_q.dtype.itemsize   # bf16 gamma for FP8 rows
         if w.head_dim:   # headwise: one shared [head_dim] gamma per tensor
@@ -90,14 +95,17 @@ class FusedStep:
         self.launches = 1
 
     def __call__(self, i):
-        x, y = self.sets[i % self.n_sets]
+        xs, ys = self.sets[i % self.n_sets]
         hq, hk = self.w.hq, self.w.hk
-        if self.w.head_dim:
-            self.qk.qknorm_headwise(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.w.head_dim, 0,
-                                    y[:, :hq], y[:, hq:hq + hk])
+        if self.w.packed:
+            x, y = xs[0], ys[0]
+            q, k, oq, ok = x[:, :hq], x[:, hq:hq + hk], y[:, :hq], y[:, hq:hq + hk]
         else:
-            self.qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, self.shards,
-                                 y[:, :hq], y[:, hq:hq + hk])
+            (q, k), (oq, ok) = xs, ys
+        if self.w.head_dim:
+            self.qk.qknorm_headwise(q, k, self.gq, self.gk, self.w.eps, self.w.head_dim, 0, oq, ok)
+        else:
+            self.qk.qknorm_fused(q, k, self.gq, self.gk, self.w.eps, self.shards, oq, ok)
 
 
 class SplitStep:
