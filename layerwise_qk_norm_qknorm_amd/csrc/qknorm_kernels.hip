@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
 #include <string>
 
 #include "qknorm_internal.hpp"
@@ -683,6 +684,15 @@ using HeadKernelFn = void (*)(const HeadArgs);
 
 constexpr int64_t kMaxGrid = (int64_t)1 << 30;
 
+// Largest grid a launch uses: kMaxGrid, or a smaller cap from the
+// QKNORM_MAX_GRID environment variable (read at each launch), under which
+// blocks loop over several token groups; tests use it to run that loop.
+int64_t grid_cap() {
+  const char* e = std::getenv("QKNORM_MAX_GRID");
+  const long long v = e ? std::atoll(e) : 0;
+  return v > 0 && v < kMaxGrid ? (int64_t)v : kMaxGrid;
+}
+
 template <class IO, int MODE, bool ALIGNED>
 KernelFn pick_slots(int v) {
   switch (v) {
@@ -770,7 +780,8 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   // One block per tokens_per_block tokens; the kernel's token loop covers
   // any remainder beyond the largest grid.
   const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
-  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  const int64_t cap = grid_cap();
+  const int64_t grid = blocks < cap ? blocks : cap;
   // hipLaunchKernel returns this launch's own status (no sticky error from
   // an earlier, unrelated call is reported as ours).
   RowArgs a = args;
@@ -796,7 +807,8 @@ int launch_heads(const Plan& p, const HeadArgs& args, void* stream, std::string*
     return (int)hipErrorInvalidValue;
   }
   const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
-  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  const int64_t cap = grid_cap();
+  const int64_t grid = blocks < cap ? blocks : cap;
   HeadArgs a = args;
   void* kargs[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
