@@ -200,6 +200,17 @@ def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
     ref = oracle.qknorm_partial_stats(inp.q, inp.k, w.dtype, shards)
     got = part.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1e-5 * ref)
+    # host combine: the planes summed in rank order in float32, handed over as one plane
+    p32 = part.cpu().numpy()
+    comb = p32[0].copy()
+    for s_ in range(1, shards):
+        comb = (comb + p32[s_]).astype(np.float32)
+    c = Packed(inp, seed=7)
+    qk.qknorm_apply_with_stats(c.q, c.k, c.gq, c.gk, w.eps, torch.from_numpy(comb[None]).to(DEV), w.hq, w.hk,
+                               c.oq, c.ok)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_np(c.oq).view(np.uint8), fq.view(np.uint8))
+    assert np.array_equal(torch_to_np(c.ok).view(np.uint8), fk.view(np.uint8))
 
 
 @pytest.mark.parametrize("key", ["small_dense", "decode_t8", "tiny"])
