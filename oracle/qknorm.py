@@ -155,8 +155,9 @@ def headwise_rmsnorm(x, gamma, eps, head_dim, gamma_head_stride):
 class QKResult:
     """Oracle outputs for one call.
 
-    ``yq``/``yk``: float64 results. ``yq_bits``/``yk_bits``: the bf16 result
-    rounded once from float64 (bf16 or FP8 I/O; None for float32). ``pq``/``pk``:
+    ``yq``/``yk``: float64 results. ``yq_bits``/``yk_bits``: the result in the
+    I/O format, rounded once from float64 (bf16 bits for bf16 I/O, E4M3 bits for
+    FP8 I/O; None for float32). ``pq``/``pk``:
     float64 shard partials [S, T] (fused only, else None).
     """
 
