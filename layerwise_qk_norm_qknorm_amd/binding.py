@@ -289,8 +289,9 @@ def describe_plan(op, hq, hk, T, dtype="bf16", shards=1, ld=None, aligned=True):
     else:                  # separate arrays
         xq, xk = (1 << 32) + off, (1 << 40) + off
     yd = 1 << 44           # outputs and gamma far away from the inputs
-    oq = Operand(xq, ld, xq + yd, ld, (1 << 46) + off, hq)
-    ok = Operand(xk, ld, xk + yd, ld, (1 << 46) + (1 << 30) + off, hk)
+    goff = 0 if aligned else (4 if dtype == "f32" else 2)   # gamma: element-aligned, not 16-byte aligned
+    oq = Operand(xq, ld, xq + yd, ld, (1 << 46) + goff, hq)
+    ok = Operand(xk, ld, xk + yd, ld, (1 << 46) + (1 << 30) + goff, hk)
     buf = ctypes.create_string_buffer(512)
     _check(lib.qknorm_describe_plan(op, ctypes.byref(oq), ctypes.byref(ok), T, code, shards, buf, 512))
     return buf.value.decode()
