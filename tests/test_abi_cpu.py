@@ -178,9 +178,9 @@ def test_describe_plans_of_the_workloads():
     # rank slice: 192 chunks over one wave, 3 each, four tokens per block
     d = qk.describe_plan(OP_PARTIAL_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
     assert "path=16B" in d and "slots=3" in d and "waves/token=1" in d and "tokens/block=4" in d
-    # a single decode token is spread over 16 waves, one chunk per lane
+    # a single decode token is spread over 8 waves, two chunks per lane
     d = qk.describe_plan(OP_FUSED, 4096, 4096, 1, "bf16", 1, ld=12288)
-    assert "slots=1" in d and "waves/token=16" in d
+    assert "slots=2" in d and "waves/token=8" in d
     d = qk.describe_plan(OP_APPLY_WITH_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
     assert "apply_with_stats" in d
     d = qk.describe_plan(OP_FUSED, 256, 256, 16, "f32", 2, ld=256)
