@@ -452,6 +452,10 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
   if (r.tokens_per_block * r.tok_threads > max_threads_for_slots(r.slots, dtype, aligned)) r.tokens_per_block = 1;
   r.threads = r.tokens_per_block * r.tok_threads;
   const int groups_per_token = r.tok_threads / r.group;
+  if (groups_per_token > 64) {  // the kernel reads one group per lane of a wave
+    *why = "internal: " + std::to_string(groups_per_token) + " lane groups per token";
+    return false;
+  }
   r.lds_bytes = r.waves > 1 ? 2 * r.tokens_per_block * groups_per_token * 2 * (int)sizeof(float) : 0;
   *p = r;
   return true;

@@ -363,7 +363,7 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 
 template <class IO, int V, int MODE, bool ALIGNED>
 __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_rows(const RowArgs a) {
-  extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token][2]
+  extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token] float2 (Q, K)
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
@@ -460,33 +460,33 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         }
       } else {
         // Several waves per token: group sums meet in LDS (double-buffered
-        // by iteration, so one barrier per iteration suffices).
-        float* rb = red + ((buf * tpb + j) * gpt) * 2;
-        if ((r & (group - 1)) == 0) {
-          rb[(r >> a.log2_group) * 2 + 0] = aq;
-          rb[(r >> a.log2_group) * 2 + 1] = ak;
-        }
+        // by iteration, so one barrier per iteration suffices). Lane q of
+        // every wave then reads group q's pair (at most 64 groups per token),
+        // and each wave adds them lane by lane, group by group within a
+        // shard and then shard by shard, with no LDS wait per group.
+        float2* rb = reinterpret_cast<float2*>(red) + (buf * tpb + j) * gpt;
+        if ((r & (group - 1)) == 0) rb[r >> a.log2_group] = make_float2(aq, ak);
         __syncthreads();
-        if (MODE == MODE_STATS) {
-          if (r < a.shards && active) {
-            float pq = rb[(r * gps) * 2 + 0], pk = rb[(r * gps) * 2 + 1];
-            for (int q = 1; q < gps; ++q) {
-              pq += rb[(r * gps + q) * 2 + 0];
-              pk += rb[(r * gps + q) * 2 + 1];
-            }
-            a.partials[(int64_t)(2 * r) * a.T + t] = pq;
-            a.partials[(int64_t)(2 * r + 1) * a.T + t] = pk;
+        const int lane = tid & 63;
+        const float2 pv = rb[lane < gpt ? lane : 0];
+        float mq = 0.0f, mk = 0.0f;  // partial_stats: the sums of shard r
+        for (int sh = 0, q0 = 0; sh < a.shards; ++sh, q0 += gps) {
+          float pq = lane_read(pv.x, q0), pk = lane_read(pv.y, q0);
+          for (int q = 1; q < gps; ++q) {
+            pq += lane_read(pv.x, q0 + q);
+            pk += lane_read(pv.y, q0 + q);
           }
-        } else {
-          for (int sh = 0; sh < a.shards; ++sh) {
-            float pq = rb[(sh * gps) * 2 + 0], pk = rb[(sh * gps) * 2 + 1];
-            for (int q = 1; q < gps; ++q) {
-              pq += rb[(sh * gps + q) * 2 + 0];
-              pk += rb[(sh * gps + q) * 2 + 1];
-            }
+          if (MODE == MODE_STATS) {
+            mq = r == sh ? pq : mq;
+            mk = r == sh ? pk : mk;
+          } else {
             ssq = sh == 0 ? pq : ssq + pq;
             ssk = sh == 0 ? pk : ssk + pk;
           }
+        }
+        if (MODE == MODE_STATS && r < a.shards && active) {
+          a.partials[(int64_t)(2 * r) * a.T + t] = mq;
+          a.partials[(int64_t)(2 * r + 1) * a.T + t] = mk;
         }
         buf ^= 1;
       }
@@ -501,7 +501,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
 
     if constexpr (MODE != MODE_STATS) {
-      if (IO::kBytes < 4 && V > 4) {  // at most 4 slots stay widened in registers
+      // Packed rows widened once for the sums are widened again for the
+      // scaling above a few slots (bf16: 2, FP8: 4), so that only the packed
+      // words stay live across the exchange: fewer registers, more waves.
+      if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
@@ -585,7 +588,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     acc = group_sum<IO::kSwap>(acc, L);
 
     {
-      if (IO::kBytes < 4 && V > 4) {
+      if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
@@ -665,7 +668,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     for (int i = 0; i < V; ++i) ss[i] = group_sum<IO::kSwap>(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
 
     {
-      if (IO::kBytes < 4 && V > 4) {
+      if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
