@@ -185,9 +185,29 @@ def test_rank_slice_partial_and_apply():
 # ----------------------------------------------------------------------- bitwise properties
 @pytest.mark.parametrize("key,shards", [("tiny", 2), ("small_dense", 4), ("decode_t64", 8), ("decode_t1", 2), ("decode_t256", 4)])
 def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
-    w = I.WORKLOADS[key]
     _log(f"[case] fused == split {key} S={shards}")
-    inp = I.make_inputs(w)
+    _check_fused_equals_split(I.make_inputs(I.WORKLOADS[key]), shards)
+
+
+@pytest.mark.parametrize("dtype,shards", [("bf16", 64), ("bf16", 32), ("bf16", 16), ("f32", 64)])
+def test_many_shards_fused_equals_partial_stats_plus_apply_bitwise(dtype, shards):
+    """Narrow shards (4 to 16 lanes each) put 16 to 64 lane groups of one
+    token through the cross-wave exchange, the most it takes; partial_stats
+    picks each shard's sum out of the same exchange."""
+    inp = I.make_custom(13, 4096, 1024, 512, dtype, seed=60 + shards)
+    w = inp.workload
+    _log(f"[case] fused == split custom {dtype} S={shards} "
+         f"plan: {qk.describe_plan(0, w.hq, w.hk, w.T, dtype, shards, ld=w.ld)}")
+    fq, fk = _check_fused_equals_split(inp, shards)
+    _compare(w, fq, fk, oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, dtype, w.eps, shards),
+             f"custom S={shards}")
+
+
+def _check_fused_equals_split(inp, shards):
+    """Fused == partial_stats + apply (S planes) == partial_stats + float32
+    combine in rank order + apply (one plane), bit for bit; the partials
+    against the oracle."""
+    w = inp.workload
     a = Packed(inp, seed=5)
     fq, fk = a.fused(shards)
     b = Packed(inp, seed=6)
@@ -211,6 +231,7 @@ def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
     torch.cuda.synchronize()
     assert np.array_equal(torch_to_np(c.oq).view(np.uint8), fq.view(np.uint8))
     assert np.array_equal(torch_to_np(c.ok).view(np.uint8), fk.view(np.uint8))
+    return fq, fk
 
 
 @pytest.mark.parametrize("key", ["small_dense", "decode_t8", "tiny"])
