@@ -348,6 +348,14 @@ __device__ __forceinline__ float swap_add32(float v) {  // lanes i ^ 32
 
 template <bool SWAP>
 __device__ __forceinline__ float group_sum(float v, int group) {
+  if (group == 64) {  // a whole wave (the common case): the same steps, no test per step
+    v += dpp_move<0xB1>(v);
+    v += dpp_move<0x4E>(v);
+    v += dpp_move<0x141>(v);
+    v += dpp_move<0x140>(v);
+    v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
+    return SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
+  }
   if (group > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
   if (group > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
   if (group > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
