@@ -346,23 +346,31 @@ __device__ __forceinline__ float swap_add32(float v) {  // lanes i ^ 32
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+template <bool SWAP, int GROUP>
+__device__ __forceinline__ float group_sum_of(float v) {
+  if (GROUP > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
+  if (GROUP > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
+  if (GROUP > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
+  if (GROUP > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
+  if (GROUP > 16) v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
+  if (GROUP > 32) v = SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
+  return v;
+}
+
+// The group width is uniform over the launch: one test picks the straight
+// sequence of steps (a test per step compiled to a branch and a
+// materialised condition each, for every token).
 template <bool SWAP>
 __device__ __forceinline__ float group_sum(float v, int group) {
-  if (group == 64) {  // a whole wave (the common case): the same steps, no test per step
-    v += dpp_move<0xB1>(v);
-    v += dpp_move<0x4E>(v);
-    v += dpp_move<0x141>(v);
-    v += dpp_move<0x140>(v);
-    v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
-    return SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
+  if (group == 64) return group_sum_of<SWAP, 64>(v);  // most launches: tested first
+  switch (group) {
+    case 32: return group_sum_of<SWAP, 32>(v);
+    case 16: return group_sum_of<SWAP, 16>(v);
+    case 8: return group_sum_of<SWAP, 8>(v);
+    case 4: return group_sum_of<SWAP, 4>(v);
+    case 2: return group_sum_of<SWAP, 2>(v);
+    default: return v;
   }
-  if (group > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
-  if (group > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
-  if (group > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
-  if (group > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
-  if (group > 16) v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
-  if (group > 32) v = SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
-  return v;
 }
 
 __device__ __forceinline__ float lane_read(float v, int lane) {
