@@ -72,8 +72,8 @@
  * elements) on the 16-byte path, and about 4096 / 6144 / 2048 chunks on the
  * element-wise path. With S > 1 shards each shard takes a power-of-two lane
  * group of at most 1024/S lanes, so a shard holds proportionally fewer.
- * QKNORM_ERR_HIP
- * means a HIP runtime call failed. qknorm_last_error() gives the message.
+ * QKNORM_ERR_HIP means a HIP runtime call failed. qknorm_last_error() gives
+ * the message.
  * Faults inside kernels surface at the caller's next synchronization. T == 0
  * is a no-op that returns QKNORM_OK after the scalar arguments are checked.
  * Pointers must be aligned to their element size (bf16 and bf16 gamma: 2
