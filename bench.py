@@ -439,7 +439,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the kernels run on one GPU; --gpus {args.gpus} is not supported "
               "(the path would shard by exchanging 2 float32 sums per token per rank, not implemented here)",
               file=sys.stderr)
         sys.exit(2)
