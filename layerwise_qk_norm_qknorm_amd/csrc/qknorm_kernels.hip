@@ -43,20 +43,14 @@ namespace {
 // I/O types. kVW: elements per 16-byte row chunk; kBytes: bytes per row
 // element; kGW / kGBytes: 32-bit words of gamma per chunk and bytes per gamma
 // element (FP8 rows take bf16 gamma).
-// kSwap: the 16- and 32-lane steps of the lane sums use permlane swaps (else
-// the LDS crossbar); chosen per type by measurement on MI355X (the swaps
-// were faster for bf16 rows, slower for FP8 rows).
 struct BF16 {
   static constexpr int kVW = 8, kBytes = 2, kGW = 4, kGBytes = 2, kDtype = kDtypeBF16;
-  static constexpr bool kSwap = true;
 };
 struct F32 {
   static constexpr int kVW = 4, kBytes = 4, kGW = 4, kGBytes = 4, kDtype = kDtypeF32;
-  static constexpr bool kSwap = true;
 };
 struct FP8 {  // OCP FP8 E4M3 (E4M3FN) rows, bf16 gamma
   static constexpr int kVW = 16, kBytes = 1, kGW = 8, kGBytes = 2, kDtype = kDtypeFP8;
-  static constexpr bool kSwap = false;
 };
 
 template <int W>
@@ -324,12 +318,12 @@ __device__ __forceinline__ void keep_packed(Words<W>& c) {
 // lane of a group ends with the same value. Inside a 16-lane row the steps
 // are DPP moves fused into the adds (quad permutes, then the half-row and
 // row mirrors, which pair lanes of the two halves once each half is
-// uniform). The 16- and 32-lane steps cross rows either through the LDS
-// crossbar or with gfx950's permlane swaps: swapping the odd rows (or the
-// upper half) of one copy with the even rows (lower half) of another leaves
-// row pairs (halves) side by side in the two results, so one add gives every
-// lane the pair's sum. Both give the same bits. Each step adds
-// two lanes' values, a + b on one and b + a (or a + b) on the other, so all
+// uniform). The 16- and 32-lane steps cross rows with gfx950's permlane
+// swaps (measured faster than the LDS crossbar for every I/O type):
+// swapping the odd rows (or the upper half) of one copy with the even rows
+// (lower half) of another leaves row pairs (halves) side by side in the two
+// results, so one add gives every lane the pair's sum. Each step adds two
+// lanes' values, a + b on one and b + a (or a + b) on the other, so all
 // lanes of a group hold bitwise the same sum.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
@@ -346,29 +340,28 @@ __device__ __forceinline__ float swap_add32(float v) {  // lanes i ^ 32
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <bool SWAP, int GROUP>
+template <int GROUP>
 __device__ __forceinline__ float group_sum_of(float v) {
   if (GROUP > 1) v += dpp_move<0xB1>(v);    // lanes i ^ 1   (quad_perm 1,0,3,2)
   if (GROUP > 2) v += dpp_move<0x4E>(v);    // lanes i ^ 2   (quad_perm 2,3,0,1)
   if (GROUP > 4) v += dpp_move<0x141>(v);   // lanes 7 - i within 8 (row_half_mirror)
   if (GROUP > 8) v += dpp_move<0x140>(v);   // lanes 15 - i within 16 (row_mirror)
-  if (GROUP > 16) v = SWAP ? swap_add16(v) : v + __shfl_xor(v, 16);
-  if (GROUP > 32) v = SWAP ? swap_add32(v) : v + __shfl_xor(v, 32);
+  if (GROUP > 16) v = swap_add16(v);
+  if (GROUP > 32) v = swap_add32(v);
   return v;
 }
 
 // The group width is uniform over the launch: one test picks the straight
 // sequence of steps (a test per step compiled to a branch and a
 // materialised condition each, for every token).
-template <bool SWAP>
 __device__ __forceinline__ float group_sum(float v, int group) {
-  if (group == 64) return group_sum_of<SWAP, 64>(v);  // most launches: tested first
+  if (group == 64) return group_sum_of<64>(v);  // most launches: tested first
   switch (group) {
-    case 32: return group_sum_of<SWAP, 32>(v);
-    case 16: return group_sum_of<SWAP, 16>(v);
-    case 8: return group_sum_of<SWAP, 8>(v);
-    case 4: return group_sum_of<SWAP, 4>(v);
-    case 2: return group_sum_of<SWAP, 2>(v);
+    case 32: return group_sum_of<32>(v);
+    case 16: return group_sum_of<16>(v);
+    case 8: return group_sum_of<8>(v);
+    case 4: return group_sum_of<4>(v);
+    case 2: return group_sum_of<2>(v);
     default: return v;
   }
 }
@@ -453,8 +446,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         ak += isq[i] ? 0.0f : cs;
       }
       // Across the lanes of a group: every lane ends with the group's sum.
-      aq = group_sum<IO::kSwap>(aq, group);
-      ak = group_sum<IO::kSwap>(ak, group);
+      aq = group_sum(aq, group);
+      ak = group_sum(ak, group);
       if (G <= 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
         // Several tokens per wave (one shard each): the group is the token.
@@ -601,7 +594,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
-    acc = group_sum<IO::kSwap>(acc, L);
+    acc = group_sum(acc, L);
 
     {
       if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
@@ -681,7 +674,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float ss[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) ss[i] = group_sum<IO::kSwap>(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
+    for (int i = 0; i < V; ++i) ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
 
     {
       if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
