@@ -283,3 +283,37 @@ def test_fp8_plans_and_checks():
     assert lib.qknorm_describe_plan(OP_FUSED, ctypes.byref(q), ctypes.byref(k), 16, 2, 1, buf, 256) == 0
     q.y = q.x + 1                                          # partial in-place shift by one FP8 element
     assert fused(q, k, dtype=2) == INVALID
+
+
+def test_error_message_is_per_thread():
+    """Each thread reads the message of its own last call (the library keeps one
+    per thread): two threads fail differently, many times, interleaved."""
+    import threading
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, kind, n=200):
+        q, k = ops()
+        msgs = set()
+        barrier.wait()
+        for _ in range(n):
+            if kind == "shards":
+                rc = fused(q, k, shards=0)
+            else:
+                rc = fused(q, k, eps=-1.0)
+            assert rc == INVALID
+            msgs.add(last_error())
+        seen[name] = msgs
+
+    ts = [threading.Thread(target=worker, args=("a", "shards")), threading.Thread(target=worker, args=("b", "eps"))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert len(seen["a"]) == 1 and len(seen["b"]) == 1
+    (ma,), (mb,) = seen["a"], seen["b"]
+    assert ma != mb and "shard" in ma.lower() and "eps" in mb.lower()
+    # a successful call clears this thread's message
+    q, k = ops()
+    q.x = k.x = 0
+    assert fused(q, k, T=0) == 0 and last_error() == ""
