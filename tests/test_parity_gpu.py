@@ -552,3 +552,46 @@ def test_runs_on_the_callers_stream():
         qk.qknorm_fused(dev.q, dev.k, dev.gq, dev.gk, w.eps, 4, dev.oq, dev.ok)
     s.synchronize()
     _compare(w, torch_to_np(dev.oq), torch_to_np(dev.ok), ref, "side stream")
+
+
+def test_concurrent_callers_on_their_own_streams():
+    """Four host threads, each with its own stream and buffers, call the three
+    entry points repeatedly at the same time; every result equals the one the
+    same call gives alone (the library keeps no shared state on the launch path)."""
+    import threading
+    keys = ["small_dense", "decode_t256", "decode_t64", "tiny"]
+    cases = []
+    for n, key in enumerate(keys):
+        w = I.WORKLOADS[key]
+        inp = I.make_inputs(w)
+        a = Packed(inp, seed=40 + n)
+        fq, fk = a.fused(2)                       # alone, on the default stream
+        b = Packed(inp, seed=50 + n)
+        cases.append((w, a, b, fq, fk))
+    _log("[case] concurrent callers: " + ", ".join(keys))
+    errors = []
+    barrier = threading.Barrier(len(cases))
+
+    def worker(w, a, b, fq, fk):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                barrier.wait()
+                for _ in range(20):
+                    qk.qknorm_fused(b.q, b.k, b.gq, b.gk, w.eps, 2, b.oq, b.ok)
+                    part = qk.qknorm_partial_stats(b.q, b.k, 2)
+                    qk.qknorm_apply_with_stats(b.q, b.k, b.gq, b.gk, w.eps, part, w.hq, w.hk, b.oq, b.ok)
+            s.synchronize()
+            if not (np.array_equal(torch_to_np(b.oq).view(np.uint8), fq.view(np.uint8)) and
+                    np.array_equal(torch_to_np(b.ok).view(np.uint8), fk.view(np.uint8))):
+                errors.append(w.key)
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(f"{w.key}: {e!r}")
+
+    ts = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in ts), "a caller thread did not finish"
+    assert not errors, errors
