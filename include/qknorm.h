@@ -29,8 +29,9 @@
  *   - sum = ((partial[0] + partial[1]) + ...) + partial[S-1]   (float32);
  *   - m = fma(sum, 1/H, eps), with 1/H rounded once to float32 on the host;
  *   - r = reciprocal square root of m from the hardware's float32 rsqrt
- *     (within about one float32 ulp; m below the float32 normal range is
- *     scaled by 2^64 first and r by 2^32 after, keeping that accuracy);
+ *     (within about one float32 ulp; where m would fall below the float32
+ *     normal range it is formed from 2^64 * sum and 2^64 * eps instead, both
+ *     exact, and r is scaled back by 2^32, keeping that accuracy);
  *   - y_j = (x_j * gamma_j) * r, rounded once to the I/O type (bf16 and FP8:
  *     round to nearest even; FP8 saturates to +-448).
  *   The float32 accumulation is the paper's (Fig. 2(b) accumulates squared

@@ -294,13 +294,16 @@ __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<I
 
 // RMS factor of Eq. 1 for a global squared sum `ss`, full width H given as
 // inv_div = 1/H (rounded once on the host): r = rsq(fma(ss, 1/H, eps)) with
-// the hardware reciprocal square root (1 ulp). Arguments below the normal
-// range are scaled by 2^64 first, so the result stays accurate there too;
+// the hardware reciprocal square root (1 ulp). Where m = ss/H + eps falls
+// below the float32 normal range, a subnormal m would keep too few bits, so
+// m is formed again from ss * 2^64 and eps * 2^64 (both exact there) and r is
+// scaled back by 2^32: one rounding in the normal range, as everywhere else.
 // 0 gives +inf and +inf gives 0, as the formula does.
 __device__ __forceinline__ float rms_factor(float ss, float inv_div, float eps) {
-  const float m = __builtin_fmaf(ss, inv_div, eps);
+  float m = __builtin_fmaf(ss, inv_div, eps);
   const bool tiny = m < 1.17549435e-38f;  // false for NaN
-  const float r = __builtin_amdgcn_rsqf(tiny ? m * 0x1p64f : m);
+  if (tiny) m = __builtin_fmaf(ss * 0x1p64f, inv_div, eps * 0x1p64f);
+  const float r = __builtin_amdgcn_rsqf(m);
   return tiny ? r * 0x1p32f : r;
 }
 

@@ -497,6 +497,36 @@ def test_large_and_small_magnitudes():
     _custom_case(40, 2048, 512, 0, "f32", 2, seed=73, scale=3e8)
 
 
+def test_factor_below_the_normal_range():
+    """eps = 0 (and a subnormal float32 eps) with rows of a few nonzero elements
+    around 3e-19: every square is a normal float32, but the mean square lies
+    below the float32 normal range, so the factor is taken on the 2^64-scaled
+    value (and nothing may be flushed to zero on the way)."""
+    T, hq, hk = 8, 4096, 1024
+    rng = np.random.default_rng(91)
+    xq, xk = np.zeros((T, hq)), np.zeros((T, hk))
+    for t in range(T):
+        n = 1 + t
+        for x, h in ((xq, hq), (xk, hk)):
+            x[t, rng.choice(h, n, replace=False)] = rng.uniform(0.5, 2.0, n) * 3e-19 * rng.choice([-1.0, 1.0], n)
+    assert np.all((xq ** 2).sum(1) / hq < 1.17e-38) and np.all((xk ** 2).sum(1) / hk < 1.17e-38)
+    for dtype in ("f32", "bf16"):
+        inp = I.make_custom(T, hq, hk, 0, dtype, seed=91)
+        enc = I.to_bf16_bits if dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+        q, k = enc(xq), enc(xk)
+        for eps in (0.0, 1e-40):
+            for S in (1, 2):
+                _log(f"[case] factor below the normal range {dtype} eps={eps} S={S}")
+                xq_d, xk_d = np_to_torch(q).to(DEV), np_to_torch(k).to(DEV)
+                gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+                qk.qknorm_fused(xq_d, xk_d, gq, gk, eps, S)
+                torch.cuda.synchronize()
+                ref = oracle.qknorm_fused(q, k, inp.gamma_q, inp.gamma_k, dtype, eps, S)
+                assert np.all(np.isfinite(ref.yq)) and np.abs(ref.yq).max() > 1.0
+                _compare(inp.workload, torch_to_np(xq_d), torch_to_np(xk_d), ref,
+                         f"tiny mean square {dtype} eps={eps} S={S}")
+
+
 def test_degenerate_rows():
     """Zero rows give 0 with eps > 0 and NaN with eps = 0; a NaN in a row
     makes that tensor's row NaN; an Inf gives 0 elsewhere and NaN at the Inf."""
