@@ -36,7 +36,10 @@
  *     round to nearest even; FP8 saturates to +-448).
  *   The float32 accumulation is the paper's (Fig. 2(b) accumulates squared
  *   sums in FP32 for BF16 activations); rows whose sum of squares overflows
- *   float32 (|x| around 1e19) give 0 or NaN instead of the real result.
+ *   float32 (|x| around 1e19) give 0 or NaN instead of the real result, and
+ *   rows whose squares fall below the float32 normal range (|x| below about
+ *   1e-19) lose accuracy in the sum (with eps = 0 and |x| below about 1e-23
+ *   the squares vanish and the result is inf or NaN).
  *
  * Data layout
  * -----------
