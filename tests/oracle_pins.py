@@ -73,6 +73,43 @@ def pin_golden_bf16_rounding():
     assert list(r.yq_bits[0]) == [0x3ECD, 0x3F81]
 
 
+def pin_golden_headwise():
+    """Hand-worked headwise examples: one factor per head, gamma shared across
+    heads (stride 0) or read per column (stride head_dim); and the same row
+    under one layerwise factor, which differs."""
+    with open(GOLDEN) as f:
+        data = json.load(f)["headwise_examples"]
+    for c in data["cases"]:
+        x = np.array([c["x"]], dtype=np.float64)
+        want = np.array([[float(Decimal(v)) for v in c["y"]]])
+        y = oq.headwise_rmsnorm(x, np.array(c["gamma"], dtype=np.float64), float(c["eps"]), c["head_dim"],
+                                c["gamma_head_stride"])
+        _close(y, want, rel=4e-16)
+        # and through the top-level call (Q and K are independent)
+        r = oq.qknorm_headwise(np.asarray(x, np.float32), np.asarray(x[:, :c["head_dim"]], np.float32),
+                               np.asarray(c["gamma"], np.float32), np.asarray(c["gamma"], np.float32), "f32",
+                               np.float32(c["eps"]), c["head_dim"], c["gamma_head_stride"])
+        _close(r.yq, want, rel=4e-16)
+    lc = data["layerwise_contrast"]
+    y, _ = oq.layerwise_rmsnorm(np.array([lc["x"]], dtype=np.float64), np.array(lc["gamma"], dtype=np.float64),
+                                float(lc["eps"]))
+    _close(y, np.array([[float(Decimal(v)) for v in lc["y"]]]), rel=4e-16)
+
+
+def pin_golden_fp8_rounding():
+    """Hand-derived E4M3 roundings: nearest, ties to even (normal and
+    subnormal), the smallest subnormal, saturation at +-448, signed zero."""
+    with open(GOLDEN) as f:
+        cases = json.load(f)["fp8_e4m3_rounding"]["cases"]
+    for c in cases:
+        v = Decimal(c["value"])
+        f64 = float(v)
+        if c.get("exact_in_f64"):
+            assert Decimal(f64) == v, "tie cases must be exact in float64"
+        got = int(oq.f64_to_fp8_bits(np.array([f64]))[0])
+        assert got == int(c["bits"], 16), (c, hex(got))
+
+
 # ---------------------------------------------------------------- closed forms
 def pin_constant_vector():
     """x_j = c for all j gives y_j = c / sqrt(c^2 + eps) * gamma_j."""
@@ -384,6 +421,8 @@ def pin_fp8_top_level():
 ALL_PINS = [
     pin_golden_worked_examples,
     pin_golden_bf16_rounding,
+    pin_golden_headwise,
+    pin_golden_fp8_rounding,
     pin_constant_vector,
     pin_one_hot,
     pin_width_one,
