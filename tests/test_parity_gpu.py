@@ -18,7 +18,7 @@ import torch
 import oracle
 import layerwise_qk_norm_qknorm_amd as qk
 from layerwise_qk_norm_qknorm_amd import inputs as I
-from gpu_helpers import (DEV, Guarded, check_bf16, check_f32, fig2b_errors, np_to_torch,
+from gpu_helpers import (DEV, Guarded, check_bf16, check_f32, check_fp8, fig2b_errors, np_to_torch,
                          torch_to_np)
 
 pytestmark = pytest.mark.gpu
@@ -625,3 +625,57 @@ def test_concurrent_callers_on_their_own_streams():
         t.join(timeout=60)
     assert not any(t.is_alive() for t in ts), "a caller thread did not finish"
     assert not errors, errors
+
+
+def test_golden_worked_examples_on_the_gpu():
+    """The hand-worked examples (tests/golden/worked_examples.json: exact
+    decimals derived by hand from Eq. 1, Phase A, the split path and headwise
+    heads) through the kernels with fp32, bf16 and FP8 rows: each result within
+    the usual tolerance of the exact decimal (one bf16 / E4M3 step of its
+    single rounding; 1e-5 relative in fp32)."""
+    import json
+    from decimal import Decimal
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")) as f:
+        data = json.load(f)
+
+    def enc(a, dtype, gamma=False):
+        a = np.asarray(a, dtype=np.float64)
+        if dtype == "f32":
+            return np_to_torch(a.astype(np.float32)).to(DEV)
+        if dtype == "bf16" or gamma:
+            return np_to_torch(I.to_bf16_bits(a)).to(DEV)
+        return np_to_torch(oracle.f64_to_fp8_bits(a)).to(DEV)
+
+    def check(got, want, dtype, what):
+        want = np.asarray(want, dtype=np.float64)
+        got = torch_to_np(got)
+        if dtype == "f32":
+            check_f32(got, want, what)
+        elif dtype == "bf16":
+            check_bf16(got, oracle.f64_to_bf16_bits(want), what)
+        else:
+            check_fp8(got, oracle.f64_to_fp8_bits(want), what)
+
+    exact = lambda ys: np.array([[float(Decimal(v)) for v in ys]])
+    for dtype in ("f32", "bf16", "fp8"):
+        for ex in data["examples"]:
+            x = np.array([ex["x"]], dtype=np.float64)
+            q, k = enc(x, dtype), enc(x, dtype)
+            gq, gk = enc(ex["gamma"], dtype, gamma=True), enc(ex["gamma"], dtype, gamma=True)
+            if ex["op"] == "fused":
+                qk.qknorm_fused(q, k, gq, gk, float(ex["eps"]), ex["shards"])
+            else:
+                st = np.array(ex["stats"], dtype=np.float32)
+                stats = torch.from_numpy(np.stack([st, st], axis=1)[:, :, None].copy()).to(DEV)  # [P][2][T=1]
+                qk.qknorm_apply_with_stats(q, k, gq, gk, float(ex["eps"]), stats, ex["h_full"], ex["h_full"])
+            torch.cuda.synchronize()
+            check(q, exact(ex["y"]), dtype, f"{ex['name']} {dtype} Q")
+            check(k, exact(ex["y"]), dtype, f"{ex['name']} {dtype} K")
+        for c in data["headwise_examples"]["cases"]:
+            x = np.array([c["x"]], dtype=np.float64)
+            q, k = enc(x, dtype), enc(x, dtype)
+            g = enc(c["gamma"], dtype, gamma=True)
+            qk.qknorm_headwise(q, k, g, g, float(c["eps"]), c["head_dim"], c["gamma_head_stride"])
+            torch.cuda.synchronize()
+            check(q, exact(c["y"]), dtype, f"{c['name']} {dtype} Q")
+            check(k, exact(c["y"]), dtype, f"{c['name']} {dtype} K")
