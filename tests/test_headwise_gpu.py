@@ -103,3 +103,15 @@ def test_in_place_headwise_equals_out_of_place():
 def test_widest_heads_and_most_heads():
     _run(4, 4096 * 2, 4096, 0, "bf16", 4096, 0, seed=501)    # 512 chunks per head
     _run(3, 8 * 200, 8 * 56, 0, "bf16", 8, 8, seed=502)      # 256 heads of one chunk
+
+
+def test_tiny_heads():
+    """Heads of 1, 2 and 4 elements, each normalized on its own (a one-element
+    head gives gamma * x / sqrt(x^2 + eps), about gamma * sign(x)): the
+    element-wise path with one lane per head, shared and per-column gamma,
+    and (1029 tokens) several tokens per wave."""
+    _run(37, 64, 32, 8, "bf16", 1, 0, seed=601)
+    _run(37, 64, 32, 8, "bf16", 1, 1, seed=602)
+    _run(19, 128, 64, 0, "f32", 2, 0, seed=603)
+    _run(1029, 96, 32, 0, "bf16", 4, 4, seed=604)
+    _run(7, 200, 56, 0, "f32", 1, 1, seed=605)
