@@ -343,7 +343,9 @@ def latency_table(dev, reps=200):
     rows = []
     cases = [(I.TINY, s) for s in I.TINY.shards] + [(I.SMALL_DENSE, s) for s in I.SMALL_DENSE.shards]
     cases += [(w, s) for w in I.DECODE for s in w.shards]
+    cases += [(w, "headwise") for w in I.DECODE]   # 128-wide heads, one shared gamma per tensor
     for w, shards in cases:
+        headwise = shards == "headwise"
         inp = I.make_inputs(w)
         if w.packed:
             x = to_device(inp.qkv, dev)
@@ -353,10 +355,16 @@ def latency_table(dev, reps=200):
         else:
             args = (to_device(inp.q, dev), to_device(inp.k, dev))
             outs = (torch.zeros_like(args[0]), torch.zeros_like(args[1]))
-        gq, gk = to_device(inp.gamma_q, dev), to_device(inp.gamma_k, dev)
+        if headwise:
+            gq, gk = to_device(inp.gamma_q[:128], dev), to_device(inp.gamma_k[:128], dev)
 
-        def call():
-            qk.qknorm_fused(*args, gq, gk, w.eps, shards, *outs)
+            def call():
+                qk.qknorm_headwise(*args, gq, gk, w.eps, 128, 0, *outs)
+        else:
+            gq, gk = to_device(inp.gamma_q, dev), to_device(inp.gamma_k, dev)
+
+            def call():
+                qk.qknorm_fused(*args, gq, gk, w.eps, shards, *outs)
 
         for _ in range(20):
             call()
@@ -399,9 +407,15 @@ def latency_table(dev, reps=200):
             b.synchronize()
             graph_us.append(a.elapsed_time(b) * 1e3 / 100)
         esz = 2 if w.dtype == "bf16" else 4
-        nbytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
-        row = {"workload": w.key, "tokens": w.T, "shards": shards,
-               "plan": qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq),
+        ld = w.ld if w.packed else w.hq
+        if headwise:
+            nbytes = 2 * w.T * (w.hq + w.hk) * esz + 2 * 128 * esz
+            plan = qk.describe_headwise_plan(w.hq, w.hk, w.T, 128, w.dtype, 0, ld=ld)
+        else:
+            nbytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * esz
+            plan = qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=ld)
+        row = {"workload": w.key, "call": "qknorm_headwise" if headwise else "qknorm_fused", "tokens": w.T,
+               "shards": 1 if headwise else shards, "plan": plan,
                "single_call_us_p10": single[reps // 10], "single_call_us_median": single[reps // 2],
                "single_call_us_p90": single[(9 * reps) // 10],
                "back_to_back_us": b2b_us, "graph_replay_us": min(graph_us), "bytes": nbytes}
