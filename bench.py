@@ -425,6 +425,65 @@ def latency_table(dev, reps=200):
     return rows
 
 
+# Prefill row widths (hq, hk, hv) besides the headline GQA one, each at
+# T = 8192 in packed rows: grouped-query shapes from 1024/256 to 16384/2048
+# and one multi-head shape (5120/5120).
+PREFILL_SHAPES = ((1024, 256, 256), (2048, 512, 512), (3072, 1024, 1024), (4096, 1024, 1024),
+                  (5120, 1024, 1024), (6144, 1024, 1024), (8192, 1024, 1024), (12288, 1024, 1024),
+                  (16384, 2048, 2048), (5120, 5120, 5120))
+
+
+def shapes_table(dev, T=8192, steps=100):
+    """The fused call over the prefill row widths above, in bf16, FP8 and
+    fp32 rows, with the planner's launch for each; one JSON line per shape.
+    `us` is GPU time per call: `steps` calls over the rotating buffer sets
+    replayed from a HIP graph, best of three replays (at the narrow widths a
+    call from Python costs more host time than the kernel takes, so
+    back-to-back launches, `us_back_to_back`, do not keep the GPU busy)."""
+    import torch
+    import layerwise_qk_norm_qknorm_amd as qk
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+
+    rows = []
+    for dtype in ("bf16", "fp8", "f32"):
+        for hq, hk, hv in PREFILL_SHAPES:
+            w = I.Workload(f"prefill_{dtype}_{hq}_{hk}", f"prefill {dtype} packed [{T}, {hq + hk + hv}]", 0, T,
+                           hq, hk, hv, dtype, True, (1,))
+            step = FusedStep(w, I.make_inputs(w), dev, 1)
+            time_steps(step, 10, 300)
+            b2b = min(time_steps(step, steps, 20)[1] for _ in range(3)) / steps
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step(0)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(steps):
+                    step(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            best = None
+            for _ in range(3):
+                a.record()
+                graph.replay()
+                b.record()
+                b.synchronize()
+                t = a.elapsed_time(b) * 1e-3 / steps
+                best = t if best is None else min(best, t)
+            row = {"workload": w.key, "dtype": dtype, "tokens": T, "hq": hq, "hk": hk, "hv": hv,
+                   "plan": qk.describe_plan(0, hq, hk, T, dtype, 1, ld=w.ld), "us": best * 1e6,
+                   "us_back_to_back": b2b * 1e6, "bytes": step.bytes, "GBps": step.bytes / best / 1e9,
+                   "frac_of_peak": step.bytes / best / 1e9 / HBM_PEAK_GBPS}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del graph, step
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -444,6 +503,8 @@ def main():
     ap.add_argument("--traffic-copy-bytes", type=int, default=100663296)
     ap.add_argument("--latency", action="store_true",
                     help="per-call times of the tiny, small-dense and decode workloads (one JSON line each)")
+    ap.add_argument("--shapes", action="store_true",
+                    help="the fused call over a range of prefill row widths (one JSON line each)")
     ap.add_argument("--traffic-commands", default="", help="the rocprofv3 commands, recorded with the result")
     args = ap.parse_args()
 
@@ -472,6 +533,10 @@ def main():
 
     if args.latency:
         latency_table(dev)
+        return
+
+    if args.shapes:
+        shapes_table(dev)
         return
 
     if args.copy_bytes:

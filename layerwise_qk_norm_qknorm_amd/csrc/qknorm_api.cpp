@@ -369,11 +369,31 @@ static int slots_for(int v, int max) {
   return 0;
 }
 
-// Launch geometry. Measured on MI355X for the packed bf16 prefill shapes:
-// what matters most is that each lane holds few chunks (about 3) so that
-// many waves share the work of a token and the loads of many tokens overlap;
-// idle slots waste issue slots, so layouts that leave more than 1/8 of the
-// slots empty are avoided when another layout fits.
+// Launch geometry, from timings of every feasible lane layout on MI355X over
+// prefill rows of 1280 to 18432 normalized elements (bf16, FP8 and fp32,
+// T = 8192). Costs are per candidate; the cheapest wins, ties going to fewer
+// waves:
+// - chunks per lane: three is best for every row type; one is always slow
+//   (too few loads in flight); fp32 rows, whose kernel keeps its occupancy
+//   at 4 and 6 slots, are indifferent between 3, 4 and 6; bf16 pays for 6
+//   slots (5 waves per SIMD instead of 8);
+// - idle slots cost little up to a quarter of a lane's slots, much beyond;
+// - blocks of 13 or more waves are slow (fp32: 12 to 25% against 6 to 12
+//   waves), and more than 8 waves per token cost a little (a longer
+//   cross-wave sum);
+// - FP8 rows (4 waves per SIMD at 3 slots) want at most 4 waves per token:
+//   5 to 12 are 8 to 60% slower; one wave per token (several tokens to a
+//   block) and 3 waves cost a little.
+static double prefill_slot_cost(int dtype, int v) {
+  if (v == 3) return 0.0;
+  if (v == 1) return 10.0;
+  switch (dtype) {
+    case kDtypeF32: return v == 4 || v == 6 ? 0.1 : v == 2 ? 0.5 : v == 8 ? 0.8 : 1.5;
+    case kDtypeFP8: return v == 2 ? 0.25 : v == 4 ? 0.3 : v == 6 ? 0.6 : v == 8 ? 1.0 : 2.0;
+    default: return v == 4 ? 0.3 : v == 2 ? 0.5 : v == 6 ? 1.0 : 2.0;
+  }
+}
+
 bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* p, std::string* why) {
   Plan r;
@@ -424,13 +444,22 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
     const int g = shards * l;
     const int64_t waste = (int64_t)l * v - nc;
     const double wfrac = (double)waste / (double)(l * v);
-    // Prefer about 3 slots per lane, few idle slots, then fewer waves; with
-    // few tokens, spread each over more waves at 2 slots per lane (measured:
-    // a decode token of 1024 chunks is 10% faster over 8 waves x 2 slots than
-    // over 16 waves x 1 slot, whose longer cross-wave sum costs more).
-    const double score = few_tokens
-        ? (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac + 0.01 * (g / 64)
-        : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (g / 64);
+    // With few tokens, spread each over more waves at 2 slots per lane
+    // (measured: a decode token of 1024 chunks is 10% faster over 8 waves x 2
+    // slots than over 16 waves x 1 slot, whose longer cross-wave sum costs
+    // more). Otherwise follow the prefill measurements above.
+    const int waves = (g + 63) / 64;
+    double score;
+    if (few_tokens) {
+      score = (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac;
+    } else {
+      score = prefill_slot_cost(dtype, v) + (wfrac > 0.25 ? 8.0 : 2.0 * wfrac) + (waves >= 13 ? 3.0 : 0.0);
+      if (dtype == kDtypeFP8)
+        score += waves >= 5 ? 3.0 : waves == 3 ? 0.35 : waves == 1 ? 0.8 : 0.0;
+      else if (waves > 8)
+        score += 0.5;
+    }
+    score += 0.01 * waves;
     if (score < best_score) {
       best_score = score;
       best = Cand{l, v, waste};
