@@ -425,17 +425,10 @@ def latency_table(dev, reps=200):
     return rows
 
 
-# Prefill row widths (hq, hk, hv) besides the headline GQA one, each at
-# T = 8192 in packed rows: grouped-query shapes from 1024/256 to 16384/2048
-# and one multi-head shape (5120/5120).
-PREFILL_SHAPES = ((1024, 256, 256), (2048, 512, 512), (3072, 1024, 1024), (4096, 1024, 1024),
-                  (5120, 1024, 1024), (6144, 1024, 1024), (8192, 1024, 1024), (12288, 1024, 1024),
-                  (16384, 2048, 2048), (5120, 5120, 5120))
-
-
 def shapes_table(dev, T=8192, steps=100):
-    """The fused call over the prefill row widths above, in bf16, FP8 and
-    fp32 rows, with the planner's launch for each; one JSON line per shape.
+    """The fused call over the prefill row widths of `inputs.PREFILL_WIDTHS`,
+    in bf16, FP8 and fp32 rows, with the planner's launch for each; one JSON
+    line per shape.
     `us` is GPU time per call: `steps` calls over the rotating buffer sets
     replayed from a HIP graph, best of three replays (at the narrow widths a
     call from Python costs more host time than the kernel takes, so
@@ -446,9 +439,8 @@ def shapes_table(dev, T=8192, steps=100):
 
     rows = []
     for dtype in ("bf16", "fp8", "f32"):
-        for hq, hk, hv in PREFILL_SHAPES:
-            w = I.Workload(f"prefill_{dtype}_{hq}_{hk}", f"prefill {dtype} packed [{T}, {hq + hk + hv}]", 0, T,
-                           hq, hk, hv, dtype, True, (1,))
+        for hq, hk, hv in I.PREFILL_WIDTHS:
+            w = I.prefill_width(dtype, hq, hk, hv, T)
             step = FusedStep(w, I.make_inputs(w), dev, 1)
             time_steps(step, 10, 300)
             b2b = min(time_steps(step, steps, 20)[1] for _ in range(3)) / steps

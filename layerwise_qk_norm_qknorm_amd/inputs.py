@@ -90,6 +90,22 @@ RANK_SLICE_FP8 = replace(RANK_SLICE, key="rank_slice_fp8",
                          title="Rank slice, FP8 E4M3: T=16384, local 1280/256 of 5120/1024, fp8 packed [16384, 1792]",
                          dtype="fp8")
 
+# Prefill row widths (hq, hk, hv) besides the GQA prefill one, in packed
+# rows: grouped-query shapes from 1024/256 to 16384/2048 and one multi-head
+# shape (5120/5120). The planner's launch differs across them (1 to 12 waves
+# per token, 2 to 6 chunks per lane, several tokens per block at the
+# narrowest).
+PREFILL_WIDTHS = ((1024, 256, 256), (2048, 512, 512), (3072, 1024, 1024), (4096, 1024, 1024),
+                  (5120, 1024, 1024), (6144, 1024, 1024), (8192, 1024, 1024), (12288, 1024, 1024),
+                  (16384, 2048, 2048), (5120, 5120, 5120))
+
+
+def prefill_width(dtype, hq, hk, hv, T=8192):
+    """A packed prefill workload of the given widths and row type."""
+    return Workload(f"prefill_{dtype}_{hq}_{hk}", f"prefill {dtype} packed [{T}, {hq + hk + hv}]", 6, T, hq, hk, hv,
+                    dtype, True, (1,))
+
+
 WORKLOADS = {w.key: w for w in (TINY, SMALL_DENSE, *DECODE, GQA_PREFILL, RANK_SLICE, GQA_PREFILL_HEADWISE,
                                 GQA_PREFILL_FP8, RANK_SLICE_FP8)}
 

@@ -1,0 +1,60 @@
+"""GPU parity over the prefill row widths (1024/256 to 16384/2048, and
+5120/5120) in bf16, FP8 and fp32 rows: each width at T = 1024, where the
+planner makes the same launch as at T = 8192 (the layouts differ across
+widths: 1 to 12 waves per token, 2 to 6 chunks per lane, several tokens per
+block at the narrowest), every element against the float64 oracle with the
+usual acceptance, plus V columns and guard bands untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import layerwise_qk_norm_qknorm_amd as qk
+from layerwise_qk_norm_qknorm_amd import inputs as I
+from gpu_helpers import DEV, Guarded, check_bf16, check_f32, check_fp8, np_to_torch
+
+pytestmark = pytest.mark.gpu
+
+T = 1024
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qk.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("hq,hk,hv", I.PREFILL_WIDTHS)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_prefill_width(dtype, hq, hk, hv):
+    w = I.prefill_width(dtype, hq, hk, hv, T)
+    plan = qk.describe_plan(0, hq, hk, T, dtype, 1, ld=w.ld)
+    assert plan == qk.describe_plan(0, hq, hk, 8192, dtype, 1, ld=w.ld)
+    print(f"[case] fused prefill {dtype} T={T} {hq}/{hk}/{hv} plan: {plan}", flush=True)
+    inp = I.make_inputs(w)
+    src = Guarded(inp.qkv, seed=11)
+    canvas = np.random.default_rng(12).integers(0, 0x7F, inp.qkv.shape).astype(inp.qkv.dtype)
+    dst = Guarded(canvas, seed=13)
+    x, y = src.view(), dst.view()
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    qk.qknorm_fused(x[:, :hq], x[:, hq:hq + hk], gq, gk, w.eps, 1, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    out = dst.host()
+    assert src.guards_intact() and dst.guards_intact()
+    assert np.array_equal(src.host(), inp.qkv)
+    assert np.array_equal(out[:, hq + hk:].view(np.uint8), canvas[:, hq + hk:].view(np.uint8))
+    ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, dtype, w.eps, 1)
+    got_q, got_k = out[:, :hq], out[:, hq:hq + hk]
+    if dtype == "bf16":
+        check_bf16(got_q, ref.yq_bits, "Q")
+        check_bf16(got_k, ref.yk_bits, "K")
+    elif dtype == "fp8":
+        check_fp8(got_q, ref.yq_bits, "Q")
+        check_fp8(got_k, ref.yk_bits, "K")
+    else:
+        check_f32(got_q, ref.yq, "Q")
+        check_f32(got_k, ref.yk, "K")
