@@ -137,3 +137,59 @@ def test_headwise_plans_fit_their_kernels(dtype, head_dim, hq_heads, hk_heads, T
     else:
         lanes = int(f["lanes/head"])
         assert lanes & (lanes - 1) == 0 and lanes * slots >= nc and G == heads * lanes
+
+
+# The prefill launches the planner makes for the widths of inputs.PREFILL_WIDTHS
+# at T = 8192 (lanes per token, chunks per lane). Each was the fastest of every
+# feasible lane layout timed on MI355X for that width and row type, or within
+# 2.2% of it.
+PREFILL_PLANS = {
+    "bf16": [(64, 3), (128, 3), (192, 3), (256, 3), (256, 3), (320, 3), (384, 3), (448, 4), (768, 3), (448, 3)],
+    "fp8": [(32, 3), (64, 3), (128, 2), (128, 3), (128, 3), (256, 2), (192, 3), (256, 4), (192, 6), (256, 3)],
+    "f32": [(128, 3), (256, 3), (256, 4), (320, 4), (512, 3), (448, 4), (384, 6), (576, 6), (768, 6), (448, 6)],
+}
+
+
+@pytest.mark.parametrize("dtype", sorted(PREFILL_PLANS))
+def test_prefill_plans_are_the_measured_best(dtype):
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+    for (hq, hk, hv), (lanes, slots) in zip(I.PREFILL_WIDTHS, PREFILL_PLANS[dtype]):
+        f = fields(qk.describe_plan(0, hq, hk, 8192, dtype, 1, ld=hq + hk + hv))
+        assert (int(f["lanes/shard"]), int(f["slots"])) == (lanes, slots), (dtype, hq, hk, f)
+
+
+def prefill_candidates(nc, dtype):
+    """(lanes, slots, waves, idle fraction) of every feasible one-shard layout
+    of a prefill launch (T >= 1024) on the 16-byte path."""
+    out = []
+    for l in [4, 8, 16, 32] + list(range(64, 1025, 64)):
+        if l % 64 and l > 64:
+            continue
+        v = slots_for(ceil_div(nc, l), dtype, True)
+        if v and l <= max_threads(v, dtype, True):
+            out.append((l, v, ceil_div(l, 64), (l * v - nc) / (l * v)))
+    return out
+
+
+@settings(max_examples=300, deadline=None, derandomize=True)
+@given(dtype=st.sampled_from(["bf16", "f32", "fp8"]), hq=st.integers(1, 1024), hk=st.integers(1, 256),
+       T=st.sampled_from([1024, 8192, 65536]))
+def test_prefill_plans_follow_the_measured_rules(dtype, hq, hk, T):
+    """Whenever a layout without the measured slow features fits, the planner
+    avoids them: one chunk per lane, more than a quarter of the slots idle,
+    blocks of 13 or more waves, and FP8 tokens over 5 or more waves."""
+    vw = VW[dtype]
+    hq, hk = hq * vw, hk * vw
+    nc = (hq + hk) // vw
+    f = fields(qk.describe_plan(0, hq, hk, T, dtype, 1))
+    l, v = int(f["lanes/shard"]), int(f["slots"])
+    waves, idle = ceil_div(l, 64), (l * v - nc) / (l * v)
+    cands = prefill_candidates(nc, dtype)
+    assert (l, v) in [(c[0], c[1]) for c in cands]
+
+    def good(c):
+        ok = c[1] > 1 and c[3] <= 0.25 and c[2] < 13
+        return ok and (c[2] <= 4 if dtype == "fp8" else True)
+
+    if any(good(c) for c in cands):
+        assert good((l, v, waves, idle)), (dtype, hq, hk, T, f)
