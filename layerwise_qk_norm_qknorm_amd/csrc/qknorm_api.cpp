@@ -372,7 +372,7 @@ static int slots_for(int v, int max) {
 // Launch geometry, from timings of every feasible lane layout on MI355X over
 // prefill rows of 1280 to 18432 normalized elements (bf16, FP8 and fp32,
 // T = 8192). Costs are per candidate; the cheapest wins, ties going to fewer
-// waves:
+// waves (launches of few tokens are scored on their own, below):
 // - chunks per lane: three is best for every row type; one is always slow
 //   (too few loads in flight); fp32 rows, whose kernel keeps its occupancy
 //   at 4 and 6 slots, are indifferent between 3, 4 and 6; bf16 pays for 6
@@ -444,22 +444,26 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
     const int g = shards * l;
     const int64_t waste = (int64_t)l * v - nc;
     const double wfrac = (double)waste / (double)(l * v);
-    // With few tokens, spread each over more waves at 2 slots per lane
-    // (measured: a decode token of 1024 chunks is 10% faster over 8 waves x 2
-    // slots than over 16 waves x 1 slot, whose longer cross-wave sum costs
-    // more). Otherwise follow the prefill measurements above.
+    // With few tokens, spread each over more waves at 2 slots per lane, but
+    // over at most 8 waves, and on a tie over more waves (timed under graph
+    // replay for T = 1 to 256 and rows of 2560 to 18432 elements: a decode
+    // token of 1024 chunks is 10% faster over 8 waves x 2 slots than over 16
+    // waves x 1 slot, and 1152 chunks 7-12% faster over 6-7 waves x 3 slots
+    // than over 9 waves x 2, whose longer cross-wave sums cost more).
+    // Otherwise follow the prefill measurements above.
     const int waves = (g + 63) / 64;
     double score;
     if (few_tokens) {
-      score = (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac;
+      score = (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac + (waves > 8 ? 1.5 : 0.0) -
+              0.01 * waves;
     } else {
       score = prefill_slot_cost(dtype, v) + (wfrac > 0.25 ? 8.0 : 2.0 * wfrac) + (waves >= 13 ? 3.0 : 0.0);
       if (dtype == kDtypeFP8)
         score += waves >= 5 ? 3.0 : waves == 3 ? 0.35 : waves == 1 ? 0.8 : 0.0;
       else if (waves > 8)
         score += 0.5;
+      score += 0.01 * waves;
     }
-    score += 0.01 * waves;
     if (score < best_score) {
       best_score = score;
       best = Cand{l, v, waste};

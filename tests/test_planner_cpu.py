@@ -193,3 +193,33 @@ def test_prefill_plans_follow_the_measured_rules(dtype, hq, hk, T):
 
     if any(good(c) for c in cands):
         assert good((l, v, waves, idle)), (dtype, hq, hk, T, f)
+
+
+# Few-token launches (lanes per token, chunks per lane), each the fastest
+# layout timed under graph replay on MI355X or within 2.9% of it.
+DECODE_PLANS = [("bf16", 4096, 4096, 512, 2), ("bf16", 8192, 1024, 384, 3), ("bf16", 2048, 512, 192, 2),
+                ("fp8", 16384, 2048, 384, 3), ("fp8", 5120, 1024, 192, 2), ("fp8", 2048, 512, 192, 1)]
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256])
+def test_decode_plans_are_the_measured_best(T):
+    for dtype, hq, hk, lanes, slots in DECODE_PLANS:
+        f = fields(qk.describe_plan(0, hq, hk, T, dtype, 1))
+        assert (int(f["lanes/shard"]), int(f["slots"])) == (lanes, slots), (dtype, hq, hk, T, f)
+
+
+@settings(max_examples=300, deadline=None, derandomize=True)
+@given(dtype=st.sampled_from(["bf16", "f32", "fp8"]), hq=st.integers(1, 1024), hk=st.integers(1, 256),
+       T=st.sampled_from([1, 8, 64, 1023]))
+def test_decode_plans_stay_within_8_waves(dtype, hq, hk, T):
+    """A few-token launch spreads a token over at most 8 waves whenever a
+    layout of at most 8 waves, at most 3 chunks per lane and at most a
+    quarter of the slots idle fits."""
+    vw = VW[dtype]
+    hq, hk = hq * vw, hk * vw
+    nc = (hq + hk) // vw
+    f = fields(qk.describe_plan(0, hq, hk, T, dtype, 1))
+    waves = ceil_div(int(f["lanes/shard"]), 64)
+    cands = [c for c in prefill_candidates(nc, dtype) if c[0] % 64 == 0]
+    if any(c[2] <= 8 and c[1] <= 3 and c[3] <= 0.25 for c in cands):
+        assert waves <= 8, (dtype, hq, hk, T, f)
