@@ -526,6 +526,13 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
   // A head of a power-of-two number of chunks (<= 64) fits an aligned lane
   // group, so the token's chunks can be laid out as in the layerwise kernel
   // (consecutive chunks on consecutive lanes), a slot per lane group per head.
+  //
+  // Token width G for prefill launches, from timings of every feasible G on
+  // MI355X (prefill rows of 1280 to 18432 elements in 64- and 128-wide heads,
+  // bf16, FP8 and fp32, T = 8192). With no exchange across waves, bf16 and
+  // fp32 rows run best over as many waves as fit (up to 16) at 2 to 6 chunks
+  // per lane with at most a quarter of the slots idle; FP8 rows (4 waves per
+  // SIMD at 3 chunks) over 2 to 4 waves, 5 or more being 8-20% slower.
   const int64_t total = heads * nc;
   if ((nc & (nc - 1)) == 0 && nc <= 64 && total <= (int64_t)kMaxThreads * 8) {
     int best_g = 0, best_v = 0;
@@ -534,9 +541,17 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
       const int v = slots_for((int)((total + g - 1) / g), max_slots(dtype, aligned));
       if (!v || g > max_threads_for_slots(v, dtype, aligned)) continue;
       const double wfrac = (double)((int64_t)g * v - total) / (double)(g * v);
-      const double score = few_tokens
-          ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
-          : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (g / 64);
+      const int waves = g / 64;
+      double score;
+      if (few_tokens) {
+        score = (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac;
+      } else if (dtype == kDtypeFP8) {
+        score = (v == 2 ? 0.0 : v == 3 ? 0.1 : v == 4 ? 0.2 : v == 6 ? 0.3 : v == 8 ? 0.6 : v == 1 ? 1.0 : 2.0) +
+                (wfrac > 0.25 ? 8.0 : 2.0 * wfrac) + (waves >= 5 ? 3.0 : waves == 1 ? 0.8 : 0.0) - 0.1 * waves;
+      } else {
+        score = (v == 2 ? 0.0 : v == 3 ? 0.05 : v == 4 ? 0.1 : v == 6 ? 0.2 : v == 8 ? 1.0 : 2.0) +
+                (wfrac > 0.25 ? 8.0 : 0.5 * wfrac) - 0.1 * waves;
+      }
       if (score < best_score) {
         best_score = score;
         best_g = g;

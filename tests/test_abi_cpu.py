@@ -251,9 +251,11 @@ def test_headwise_rejects():
 
 
 def test_headwise_plans():
-    # heads of 16 chunks: token-wide layout, 768 chunks over 256 lanes, a 16-lane group per head
+    # heads of 16 chunks: token-wide layout, 768 chunks over 512 lanes (8 waves, 2 slots), a 16-lane
+    # group per head
     d = qk.describe_headwise_plan(5120, 1024, 8192, 128, ld=7168)
-    assert "heads=(40,8)" in d and "layout=token-wide" in d and "lanes/head=16" in d and "slots=3" in d
+    assert "heads=(40,8)" in d and "layout=token-wide" in d and "lanes/head=16" in d and "slots=2" in d
+    assert "threads/token=512" in d
     # heads of 18 fp32 chunks (not a power of two): one lane group per head
     d = qk.describe_headwise_plan(576, 144, 33, 72, "f32")
     assert "layout=per-head" in d

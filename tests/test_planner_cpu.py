@@ -223,3 +223,22 @@ def test_decode_plans_stay_within_8_waves(dtype, hq, hk, T):
     cands = [c for c in prefill_candidates(nc, dtype) if c[0] % 64 == 0]
     if any(c[2] <= 8 and c[1] <= 3 and c[3] <= 0.25 for c in cands):
         assert waves <= 8, (dtype, hq, hk, T, f)
+
+
+# Headwise prefill launches for 128-wide heads over the same widths (threads
+# per token, chunks per lane): each the fastest token width timed on MI355X
+# or within 3.4% of it. The narrowest rows, where every width timed the same
+# (host-bound launches), are pinned as they are.
+HEADWISE_PREFILL_PLANS = {
+    "bf16": [(64, 3), (192, 2), (256, 2), (384, 2), (512, 2), (576, 2), (768, 2), (1024, 2), (1024, 3), (832, 2)],
+    "fp8": [(256, 1), (192, 1), (128, 2), (192, 2), (192, 2), (256, 2), (192, 3), (256, 4), (192, 6), (256, 3)],
+    "f32": [(192, 2), (384, 2), (640, 2), (832, 2), (1024, 2), (1024, 2), (1024, 3), (1024, 4), (1024, 6), (1024, 3)],
+}
+
+
+@pytest.mark.parametrize("dtype", sorted(HEADWISE_PREFILL_PLANS))
+def test_headwise_prefill_plans_are_the_measured_best(dtype):
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+    for (hq, hk, hv), (threads, slots) in zip(I.PREFILL_WIDTHS, HEADWISE_PREFILL_PLANS[dtype]):
+        f = fields(qk.describe_headwise_plan(hq, hk, 8192, 128, dtype, 0, ld=hq + hk + hv))
+        assert (int(f["threads/token"]), int(f["slots"])) == (threads, slots), (dtype, hq, hk, f)
