@@ -582,9 +582,23 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
     const int64_t threads = (g + 63) / 64 * 64;
     if (threads > max_threads_for_slots(v, dtype, aligned)) continue;
     const double wfrac = (double)((int64_t)l * v - nc) / (double)(l * v);
-    const double score = few_tokens
-        ? (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac
-        : (v > 3 ? (v - 3) : (3 - v)) + (wfrac > 0.125 ? 8.0 : 0.0) + 4.0 * wfrac + 0.01 * (double)threads / 64;
+    // Prefill: from timings of every lane group on MI355X (heads of 80 and 96
+    // columns, 40 to 128 heads per token, T = 8192), the best chunks per lane
+    // are 2 for bf16 rows (8 lanes per head: 7-52% faster than 4 lanes x 3
+    // chunks, idle slots notwithstanding), 1 for FP8 rows up to 512 threads
+    // per token (else 2), and 3 for fp32 rows.
+    double score;
+    if (few_tokens) {
+      score = (double)v + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac;
+    } else {
+      if (dtype == kDtypeBF16)
+        score = v == 2 ? 0.0 : (v == 1 || v == 3) ? 0.5 : 1.0 + 0.1 * v;
+      else if (dtype == kDtypeFP8)
+        score = (v == 1 ? 0.0 : v == 2 ? 0.2 : 1.0 + 0.1 * v) + (threads >= 640 ? 0.5 : 0.0);
+      else
+        score = v == 3 ? 0.0 : v == 2 ? 0.2 : v == 4 ? 0.3 : 1.0 + 0.1 * v;
+      score += wfrac > 0.5 ? 8.0 : wfrac;
+    }
     if (score < best_score) {
       best_score = score;
       best_l = l;

@@ -246,3 +246,21 @@ def test_fp8_headwise_head_sizes(head_dim, stride):
     ref = oracle.qknorm_headwise(inp.q, inp.k, gq_h, gk_h, "fp8", 1e-6, head_dim, stride)
     check_fp8(torch_to_np(oq), ref.yq_bits, "headwise fp8 Q")
     check_fp8(torch_to_np(ok), ref.yk_bits, "headwise fp8 K")
+
+
+@pytest.mark.parametrize("head_dim,hq,hk", [(96, 3072, 768), (96, 9216, 1536), (80, 5120, 1280), (128, 16384, 2048)])
+def test_fp8_headwise_prefill_layouts(head_dim, hq, hk):
+    """Prefill launches of FP8 rows (T = 1024, the T = 8192 layouts): per-head
+    lane groups of 1 and 2 chunks per lane, and a token-wide layout of 6 chunks."""
+    T = 1024
+    inp = I.make_custom(T, hq, hk, 0, "fp8", seed=1300 + head_dim + hq // 64)
+    gq_h, gk_h = inp.gamma_q[:head_dim].copy(), inp.gamma_k[:head_dim].copy()
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    oq, ok = torch.empty_like(xq), torch.empty_like(xk)
+    _log(f"[case] fp8 headwise prefill head_dim={head_dim} {hq}/{hk} plan: "
+         f"{qk.describe_headwise_plan(hq, hk, T, head_dim, 'fp8', 0)}")
+    qk.qknorm_headwise(xq, xk, np_to_torch(gq_h).to(DEV), np_to_torch(gk_h).to(DEV), 1e-6, head_dim, 0, oq, ok)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_headwise(inp.q, inp.k, gq_h, gk_h, "fp8", 1e-6, head_dim, 0)
+    check_fp8(torch_to_np(oq), ref.yq_bits, "headwise fp8 Q")
+    check_fp8(torch_to_np(ok), ref.yk_bits, "headwise fp8 K")

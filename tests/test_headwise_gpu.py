@@ -115,3 +115,13 @@ def test_tiny_heads():
     _run(19, 128, 64, 0, "f32", 2, 0, seed=603)
     _run(1029, 96, 32, 0, "bf16", 4, 4, seed=604)
     _run(7, 200, 56, 0, "f32", 1, 1, seed=605)
+
+
+@pytest.mark.parametrize("head_dim,hq,hk", [(96, 3072, 768), (80, 5120, 1280), (96, 3072, 3072), (128, 12288, 1024),
+                                            (64, 4096, 1024), (128, 16384, 2048)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_head_layouts(dtype, head_dim, hq, hk):
+    """Prefill launches (T = 1024, the same layouts as at T = 8192): per-head
+    lane groups for 80- and 96-wide heads, token-wide layouts of up to 16
+    waves for 64- and 128-wide heads."""
+    _run(1024, hq, hk, hk, dtype, head_dim, 0, seed=300 + head_dim + hq // 64)

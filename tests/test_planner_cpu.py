@@ -242,3 +242,18 @@ def test_headwise_prefill_plans_are_the_measured_best(dtype):
     for (hq, hk, hv), (threads, slots) in zip(I.PREFILL_WIDTHS, HEADWISE_PREFILL_PLANS[dtype]):
         f = fields(qk.describe_headwise_plan(hq, hk, 8192, 128, dtype, 0, ld=hq + hk + hv))
         assert (int(f["threads/token"]), int(f["slots"])) == (threads, slots), (dtype, hq, hk, f)
+
+
+# Per-head headwise prefill launches (heads whose chunk count is not a power
+# of two): (lanes per head, chunks per lane), each the fastest lane group
+# timed on MI355X except the fp32 3072/3072 case (within 5.2%).
+PER_HEAD_PLANS = [("bf16", 96, 3072, 768, 8, 2), ("bf16", 80, 5120, 1280, 8, 2), ("fp8", 96, 3072, 768, 8, 1),
+                  ("fp8", 96, 9216, 1536, 4, 2), ("fp8", 80, 5120, 1280, 4, 2), ("f32", 96, 6144, 768, 8, 3),
+                  ("f32", 80, 2560, 640, 8, 3), ("f32", 96, 3072, 3072, 8, 3)]
+
+
+def test_per_head_prefill_plans_are_the_measured_best():
+    for dtype, hd, hq, hk, lanes, slots in PER_HEAD_PLANS:
+        f = fields(qk.describe_headwise_plan(hq, hk, 8192, hd, dtype, 0, ld=hq + 2 * hk))
+        assert f["layout"] == "per-head"
+        assert (int(f["lanes/head"]), int(f["slots"])) == (lanes, slots), (dtype, hd, hq, hk, f)
