@@ -426,9 +426,10 @@ def latency_table(dev, reps=200):
 
 
 def shapes_table(dev, T=8192, steps=100):
-    """The fused call over the prefill row widths of `inputs.PREFILL_WIDTHS`,
-    in bf16, FP8 and fp32 rows, with the planner's launch for each; one JSON
-    line per shape.
+    """The fused call, then the headwise call (128-wide heads, one shared
+    gamma), over the prefill row widths of `inputs.PREFILL_WIDTHS` in bf16,
+    FP8 and fp32 rows, with the planner's launch for each; one JSON line per
+    shape.
     `us` is GPU time per call: `steps` calls over the rotating buffer sets
     replayed from a HIP graph, best of three replays (at the narrow widths a
     call from Python costs more host time than the kernel takes, so
@@ -437,10 +438,12 @@ def shapes_table(dev, T=8192, steps=100):
     import layerwise_qk_norm_qknorm_amd as qk
     from layerwise_qk_norm_qknorm_amd import inputs as I
 
+    from dataclasses import replace
+
     rows = []
-    for dtype in ("bf16", "fp8", "f32"):
+    for head_dim, dtype in [(0, d) for d in ("bf16", "fp8", "f32")] + [(128, d) for d in ("bf16", "fp8", "f32")]:
         for hq, hk, hv in I.PREFILL_WIDTHS:
-            w = I.prefill_width(dtype, hq, hk, hv, T)
+            w = replace(I.prefill_width(dtype, hq, hk, hv, T), head_dim=head_dim)
             step = FusedStep(w, I.make_inputs(w), dev, 1)
             time_steps(step, 10, 300)
             b2b = min(time_steps(step, steps, 20)[1] for _ in range(3)) / steps
@@ -465,8 +468,10 @@ def shapes_table(dev, T=8192, steps=100):
                 b.synchronize()
                 t = a.elapsed_time(b) * 1e-3 / steps
                 best = t if best is None else min(best, t)
-            row = {"workload": w.key, "dtype": dtype, "tokens": T, "hq": hq, "hk": hk, "hv": hv,
-                   "plan": qk.describe_plan(0, hq, hk, T, dtype, 1, ld=w.ld), "us": best * 1e6,
+            plan = (qk.describe_headwise_plan(hq, hk, T, head_dim, dtype, 0, ld=w.ld) if head_dim
+                    else qk.describe_plan(0, hq, hk, T, dtype, 1, ld=w.ld))
+            row = {"workload": w.key, "call": step.name, "head_dim": head_dim, "dtype": dtype, "tokens": T,
+                   "hq": hq, "hk": hk, "hv": hv, "plan": plan, "us": best * 1e6,
                    "us_back_to_back": b2b * 1e6, "bytes": step.bytes, "GBps": step.bytes / best / 1e9,
                    "frac_of_peak": step.bytes / best / 1e9 / HBM_PEAK_GBPS}
             rows.append(row)
@@ -496,7 +501,7 @@ def main():
     ap.add_argument("--latency", action="store_true",
                     help="per-call times of the tiny, small-dense and decode workloads (one JSON line each)")
     ap.add_argument("--shapes", action="store_true",
-                    help="the fused call over a range of prefill row widths (one JSON line each)")
+                    help="the fused and headwise calls over a range of prefill row widths (one JSON line each)")
     ap.add_argument("--traffic-commands", default="", help="the rocprofv3 commands, recorded with the result")
     args = ap.parse_args()
 
