@@ -58,8 +58,61 @@ def to_device(a, dev):
     return torch.from_numpy(a.copy()).to(dev)
 
 
+# ----------------------------------------------------------------------------- ceiling kernels
+class CeilingLib:
+    """ctypes handle of libstreamceil.so: the plain streaming copy and read
+    kernels (16-byte loads, non-temporal 16-byte stores) that give the
+    practical HBM ceiling for the bytes a QK-Norm call moves."""
+
+    def __init__(self):
+        import ctypes
+        from layerwise_qk_norm_qknorm_amd import build_lib
+        if not os.path.exists(build_lib.CEIL_LIB):
+            raise RuntimeError(f"{build_lib.CEIL_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(build_lib.CEIL_LIB)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.qkceil_stream.argtypes = [vp, i64, vp, i64, i64, i64, ci, ci, vp, vp]
+        lib.qkceil_stream.restype = ci
+        lib.qkceil_last_error.restype = ctypes.c_char_p
+        lib.qkceil_last_error.argtypes = []
+        self.lib = lib
+
+    def stream(self, x, ldx, y, ldy, rows, row_bytes, per, block, sink, stream):
+        rc = self.lib.qkceil_stream(x, ldx, y, ldy, rows, row_bytes, per, block, sink, stream)
+        if rc:
+            raise RuntimeError(f"qkceil_stream: {self.lib.qkceil_last_error().decode()}")
+
+
+# (chunks per thread, threads per block) tried for the ceiling of each call
+CEIL_CONFIGS = ((1, 256), (2, 256), (3, 256), (4, 256), (1, 512), (2, 512), (1, 1024), (2, 1024))
+
+
+def _current_stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
 # ----------------------------------------------------------------------------- steps
-class FusedStep:
+class Step:
+    """A timed unit: one library call over buffer set i % n_sets. Subclasses
+    fill `sets`, `bytes` (algorithmic bytes per call), `name`, and `spans(i)`:
+    the (x, ldx, y, ldy, rows, row_bytes) byte spans of Q/K columns that the
+    call reads (and writes) in set i, for the streaming ceiling."""
+
+    copy = True   # the call writes what it reads (False: read only)
+    launches = 1
+
+    def _rotate(self, per_set):
+        return max(1, -(-ROTATE_MIN_BYTES // per_set))
+
+
+def _packed_span(w, x, y):
+    esz = x.element_size()
+    return (x.data_ptr(), w.ld * esz, y.data_ptr() if y is not None else None, w.ld * esz, w.T,
+            (w.hq + w.hk) * esz)
+
+
+class FusedStep(Step):
     """One qknorm_fused (or qknorm_headwise) call over a buffer set: packed
     QKV rows, or separate Q and K arrays for the workloads laid out that way."""
 
@@ -74,7 +127,7 @@ class FusedStep:
             srcs = [to_device(inp.q, dev), to_device(inp.k, dev)]
             x0 = srcs[0]
         per_set = 2 * sum(t.numel() * t.element_size() for t in srcs)
-        self.n_sets = max(1, -(-ROTATE_MIN_BYTES // per_set))
+        self.n_sets = self._rotate(per_set)
         self.sets = []
         for i in range(self.n_sets):
             xs = srcs if i == 0 else [t.clone() for t in srcs]
@@ -91,8 +144,15 @@ class FusedStep:
             self.gk = to_device(inp.gamma_k, dev)
             self.bytes = 2 * w.T * (w.hq + w.hk) * esz + (w.hq + w.hk) * gsz
             self.name = "qknorm_fused"
+        self.stream_bytes = 2 * w.T * (w.hq + w.hk) * esz
         self.footprint = self.n_sets * per_set
-        self.launches = 1
+
+    def spans(self, i):
+        xs, ys = self.sets[i % self.n_sets]
+        if self.w.packed:
+            return [_packed_span(self.w, xs[0], ys[0])]
+        return [(x.data_ptr(), x.shape[1] * x.element_size(), y.data_ptr(), y.shape[1] * y.element_size(),
+                 x.shape[0], x.shape[1] * x.element_size()) for x, y in zip(xs, ys)]
 
     def __call__(self, i):
         xs, ys = self.sets[i % self.n_sets]
@@ -108,89 +168,188 @@ class FusedStep:
             self.qk.qknorm_fused(q, k, self.gq, self.gk, self.w.eps, self.shards, oq, ok)
 
 
-class SplitStep:
-    """One rank's share of the split path: qknorm_partial_stats on the local
-    slice, then qknorm_apply_with_stats with the local plane and the peer
-    planes (computed once before timing, as if received)."""
+class PartialStep(Step):
+    """qknorm_partial_stats on one rank's slice (Phase A: the local sums of
+    squares, one plane of 2 x T float32), each call on its own buffer set."""
+
+    copy = False
 
     def __init__(self, w, inp, dev):
         import torch
         import layerwise_qk_norm_qknorm_amd as qk
         self.qk, self.w = qk, w
         x0 = to_device(inp.qkv, dev)
-        per_set = 2 * x0.numel() * x0.element_size()
-        self.n_sets = max(1, -(-ROTATE_MIN_BYTES // per_set))
+        per_set = x0.numel() * x0.element_size() + 8 * w.T
+        self.n_sets = self._rotate(per_set)
+        self.sets = [(x0 if i == 0 else x0.clone(), torch.empty((1, 2, w.T), dtype=torch.float32, device=dev))
+                     for i in range(self.n_sets)]
+        esz = x0.element_size()
+        self.bytes = w.T * (w.hq + w.hk) * esz + 8 * w.T
+        self.stream_bytes = w.T * (w.hq + w.hk) * esz
+        self.footprint = self.n_sets * per_set
+        self.name = "qknorm_partial_stats"
+
+    def spans(self, i):
+        return [_packed_span(self.w, self.sets[i % self.n_sets][0], None)]
+
+    def __call__(self, i):
+        x, planes = self.sets[i % self.n_sets]
+        hq, hk = self.w.hq, self.w.hk
+        self.qk.qknorm_partial_stats(x[:, :hq], x[:, hq:hq + hk], 1, planes)
+
+
+class ApplyStep(Step):
+    """qknorm_apply_with_stats on one rank's slice: the local plane plus the
+    peers' planes (computed once before timing, as if received), added in
+    rank order, full widths as divisors (Phase B and the final scaling), each
+    call on its own buffer set."""
+
+    def __init__(self, w, inp, dev):
+        import torch
+        import layerwise_qk_norm_qknorm_amd as qk
+        self.qk, self.w = qk, w
+        x0 = to_device(inp.qkv, dev)
         P = inp.peer_q.shape[0]
-        self.sets = []
-        for i in range(self.n_sets):
-            x = x0 if i == 0 else x0.clone()
-            y = torch.zeros_like(x0)
-            planes = torch.empty((1 + P, 2, w.T), dtype=torch.float32, device=dev)
-            self.sets.append((x, y, planes))
+        planes0 = torch.empty((1 + P, 2, w.T), dtype=torch.float32, device=dev)
+        qk.qknorm_partial_stats(x0[:, :w.hq], x0[:, w.hq:w.hq + w.hk], 1, planes0[0:1])
         for p in range(P):
             pq, pk = to_device(inp.peer_q[p], dev), to_device(inp.peer_k[p], dev)
-            part = qk.qknorm_partial_stats(pq, pk, 1)
-            for s in self.sets:
-                s[2][1 + p].copy_(part[0])
+            qk.qknorm_partial_stats(pq, pk, 1, planes0[1 + p:2 + p])
+        per_set = 2 * x0.numel() * x0.element_size() + planes0.numel() * 4
+        self.n_sets = self._rotate(per_set)
+        self.sets = [(x0 if i == 0 else x0.clone(), torch.zeros_like(x0), planes0.clone())
+                     for i in range(self.n_sets)]
         self.gq = to_device(inp.gamma_q, dev)
         self.gk = to_device(inp.gamma_k, dev)
         esz = x0.element_size()
         gsz = inp.gamma_q.dtype.itemsize
         h = w.hq + w.hk
-        self.bytes_partial = w.T * h * esz + 8 * w.T
-        self.bytes_apply = 2 * w.T * h * esz + 8 * (1 + P) * w.T + h * gsz
-        self.bytes = self.bytes_partial + self.bytes_apply
+        self.bytes = 2 * w.T * h * esz + 8 * (1 + P) * w.T + h * gsz
+        self.stream_bytes = 2 * w.T * h * esz
         self.footprint = self.n_sets * per_set
-        self.launches = 2
-        self.name = "qknorm_partial_stats+qknorm_apply_with_stats"
+        self.name = "qknorm_apply_with_stats"
+
+    def spans(self, i):
+        x, y, _ = self.sets[i % self.n_sets]
+        return [_packed_span(self.w, x, y)]
 
     def __call__(self, i):
         x, y, planes = self.sets[i % self.n_sets]
         hq, hk = self.w.hq, self.w.hk
-        self.qk.qknorm_partial_stats(x[:, :hq], x[:, hq:hq + hk], 1, planes[0:1])
         self.qk.qknorm_apply_with_stats(x[:, :hq], x[:, hq:hq + hk], self.gq, self.gk, self.w.eps, planes,
                                         self.w.hq_full, self.w.hk_full, y[:, :hq], y[:, hq:hq + hk])
 
 
-class CopyStep:
-    """A plain device copy of a known byte count (calibration for the
-    hardware counters and the practical bandwidth ceiling)."""
+class CeilingStep(Step):
+    """The streaming ceiling of a call: a plain copy (or read) of exactly the
+    Q/K column bytes that `step` moves, over the same rotating buffer sets,
+    with `per` chunks per thread and `block` threads per block."""
 
-    def __init__(self, nbytes, dev):
-        import torch
-        n = nbytes // 2
-        self.sets = [(torch.ones(n, dtype=torch.bfloat16, device=dev), torch.empty(n, dtype=torch.bfloat16,
-                                                                                   device=dev))
-                     for _ in range(max(1, -(-ROTATE_MIN_BYTES // (2 * nbytes))))]
-        self.n_sets = len(self.sets)
-        self.bytes = 2 * n * 2
-        self.footprint = self.n_sets * 2 * nbytes
-        self.launches = 1
-        self.name = "copy"
+    def __init__(self, step, lib, per, block, sink):
+        self.step, self.lib, self.per, self.block, self.sink = step, lib, per, block, sink
+        self.n_sets = step.n_sets
+        self.copy = step.copy
+        self.bytes = step.stream_bytes
+        self.launches = len(step.spans(0))
+        self.name = f"stream_{'copy' if step.copy else 'read'}(per={per}, block={block})"
 
     def __call__(self, i):
+        st = _current_stream()
+        for x, ldx, y, ldy, rows, row_bytes in self.step.spans(i):
+            self.lib.stream(x, ldx, y if self.copy else None, ldy, rows, row_bytes, self.per, self.block,
+                            self.sink, st)
+
+
+class ContiguousCopy(Step):
+    """Buffers of `nbytes` copied (or read) whole: the plain device copy of a
+    known byte count, for the counter calibration and the ceiling table."""
+
+    def __init__(self, nbytes, dev, copy=True):
+        import torch
+        n = nbytes // 16 * 16
+        self.copy = copy
+        per_set = 2 * n if copy else n
+        self.n_sets = self._rotate(per_set)
+        self.sets = [(torch.ones(n // 2, dtype=torch.bfloat16, device=dev),
+                      torch.empty(n // 2, dtype=torch.bfloat16, device=dev) if copy else None)
+                     for _ in range(self.n_sets)]
+        self.stream_bytes = self.bytes = (2 if copy else 1) * n
+        self.n = n
+        self.footprint = self.n_sets * per_set
+        self.name = "contiguous " + ("copy" if copy else "read")
+
+    def spans(self, i):
         a, b = self.sets[i % self.n_sets]
-        b.copy_(a)
+        return [(a.data_ptr(), self.n, b.data_ptr() if b is not None else None, self.n, 1, self.n)]
 
 
 # ----------------------------------------------------------------------------- timing
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, graph=True):
+    """Runs `warmup` untimed calls, then times exactly `steps` calls: wall
+    clock and HIP events on the launch stream (the current stream, which the
+    binding launches on), with a device synchronization on both sides.
+
+    graph=True: the `steps` calls are captured once in a HIP graph, which is
+    replayed once untimed (its first launch uploads it) and then once timed,
+    so the events see the kernels back to back, not the host's pace (a call
+    through the Python binding costs about 8 us of host time, more than some
+    of these kernels take). graph=False: eager calls from Python."""
     import torch
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        step(warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    step(warmup + i)
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del g
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            step(warmup + i)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ev_ms = start.elapsed_time(end)
     return wall, ev_ms / 1000.0
+
+
+def ceiling_sweep(step, dev, steps=200, warmup=100, configs=CEIL_CONFIGS, verbose=True, graph=True):
+    """Times the streaming copy (or read) of the bytes `step` moves for each
+    (per, block) in `configs`; returns the rows and the fastest."""
+    import torch
+    lib = CeilingLib()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rows = []
+    for per, block in configs:
+        cs = CeilingStep(step, lib, per, block, sink.data_ptr())
+        _, ev = time_steps(cs, steps, warmup, graph=graph)
+        us = ev / steps * 1e6
+        row = {"kernel": cs.name, "per": per, "block": block, "bytes": cs.bytes, "us": us,
+               "GBps": cs.bytes / (us * 1e-6) / 1e9}
+        row["frac_of_peak"] = row["GBps"] / HBM_PEAK_GBPS
+        rows.append(row)
+        if verbose:
+            log(f"[ceiling] {cs.name}: {us:.2f} us, {row['GBps']:.0f} GB/s ({row['frac_of_peak']:.3f} of peak)")
+    best = max(rows, key=lambda r: r["GBps"])
+    return rows, best
 
 
 def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
@@ -200,7 +359,10 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
 
     import oracle
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    # The GPU machine's CPU share for one GPU is 16 threads, whatever the
+    # affinity mask shows; both counts are recorded.
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, 16)
     chunk = 256
     spans = [(a, min(a + chunk, w.T)) for a in range(0, w.T, chunk)]
 
@@ -246,6 +408,7 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
         "value": tokens / el,
         "unit": "tokens/s",
         "cores": cores,
+        "affinity_cores": affinity,
         "kind": "oracle",
         "value_1_thread": tokens1 / el1,
         "sample": f"{w.key}: all {w.T} tokens x {passes} passes ({tokens} tokens, {el:.1f} s), "
@@ -254,8 +417,15 @@ def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
     }
 
 
-def load_traffic(workload, kernel_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+# rocprofv3 --pmc counters of the requests the L2 (TCC) sends to the memory
+# fabric (EA), summed over the L2 channels; two runs, one per direction (at
+# most 4 TCC counters per run).
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum")
+
+
+def load_traffic(workload, call, kernel_hash):
+    """HBM bytes per launch of `call` from the committed counter summary, if
     it was taken on the current kernel sources (else None)."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
@@ -266,65 +436,89 @@ def load_traffic(workload, kernel_hash):
         log(f"[bench] {path} was taken on kernel sources {d.get('kernel_source_hash')}, now {kernel_hash}: "
             "traffic reported as null")
         return None
-    return d.get("traffic_bytes_per_launch")
+    k = d.get("kernels", {}).get(call)
+    return k.get("traffic_bytes_per_launch") if k else None
 
 
-def _counter_rows(directory, counter):
-    """(kernel name, value) for every dispatch in the counter CSVs under `directory`."""
+def _call_of(kernel_name):
+    """The library call (or ceiling kernel) a dispatched kernel belongs to."""
+    n = kernel_name
+    if "stream_rows<" in n:
+        return "stream_copy" if n.split("stream_rows<")[1].split(">")[0].split(",")[1].strip() == "true" \
+            else "stream_read"
+    if "qknorm_heads" in n:
+        return "qknorm_headwise"
+    if "qknorm_rows<" in n:
+        mode = n.split("qknorm_rows<")[1].split(">")[0].split(",")[2].strip()
+        return {"0": "qknorm_fused", "1": "qknorm_partial_stats", "2": "qknorm_apply_with_stats"}.get(mode)
+    return None
+
+
+def _counter_medians(dirs):
+    """{call: {counter: median over its dispatches}} from rocprofv3 counter CSVs."""
     import csv
     import glob
-    rows = []
-    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
-        with open(path, newline="") as f:
-            for r in csv.DictReader(f):
-                if r.get("Counter_Name") == counter:
-                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
-    return rows
+    vals = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    call = _call_of(r.get("Kernel_Name", ""))
+                    if call:
+                        vals.setdefault(call, {}).setdefault(r["Counter_Name"], []).append(
+                            float(r["Counter_Value"]))
+    return {c: {k: sorted(v)[len(v) // 2] for k, v in cs.items()} for c, cs in vals.items()}, \
+        {c: {k: len(v) for k, v in cs.items()} for c, cs in vals.items()}
 
 
-def _median(v):
-    v = sorted(v)
-    return v[len(v) // 2] if v else None
+def request_bytes(m):
+    """Bytes the L2 requested from the fabric, from the request counters:
+    reads are 128-, 64- or 32-byte requests (TCC_BUBBLE counts the 128-byte
+    ones, TCC_EA0_RDREQ_32B the 32-byte ones, TCC_EA0_RDREQ all), writes 64-
+    or 32-byte requests (TCC_EA0_WRREQ_64B the 64-byte ones)."""
+    out = {}
+    if "TCC_EA0_RDREQ_sum" in m:
+        rd, r32, r128 = m["TCC_EA0_RDREQ_sum"], m.get("TCC_EA0_RDREQ_32B_sum", 0.0), m.get("TCC_BUBBLE_sum", 0.0)
+        out["read_bytes"] = 128.0 * r128 + 64.0 * (rd - r128 - r32) + 32.0 * r32
+    if "TCC_EA0_WRREQ_sum" in m:
+        wr, w64 = m["TCC_EA0_WRREQ_sum"], m.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+        out["write_bytes"] = 64.0 * w64 + 32.0 * (wr - w64)
+    return out
 
 
-def record_traffic(workload, d_fetch, d_write, d_copy_fetch, d_copy_write, copy_bytes, commands):
-    """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, for the
-    kernel and for a plain copy of `copy_bytes`) into HBM bytes per launch,
-    stored with the hash of the kernel sources they were taken on."""
+def record_traffic(workload, dirs, commands):
+    """Turns rocprofv3 --pmc runs of `bench.py --workload <workload>` (read
+    counters in one run, write counters in another) into HBM bytes per launch
+    for each call of the workload, checked against the streaming copy or read
+    of the same bytes in the same runs, whose byte count is known exactly."""
     from layerwise_qk_norm_qknorm_amd import inputs as I
-    med = {}
-    for key, d, ctr, pat in (("fetch", d_fetch, "FETCH_SIZE", "qknorm_rows"),
-                             ("write", d_write, "WRITE_SIZE", "qknorm_rows"),
-                             ("copy_fetch", d_copy_fetch, "FETCH_SIZE", "copy"),
-                             ("copy_write", d_copy_write, "WRITE_SIZE", "copy")):
-        vals = [v for n, v in _counter_rows(d, ctr) if pat in n]
-        if key.startswith("copy"):  # the timed copies, not set-up traffic
-            top = max(vals)
-            vals = [v for v in vals if v > 0.5 * top]
-        med[key] = _median(vals)
-        log(f"[traffic] {key}: {len(vals)} dispatches, median {med[key]} KiB")
-    f_scale = copy_bytes / (med["copy_fetch"] * 1024.0)
-    w_scale = copy_bytes / (med["copy_write"] * 1024.0)
+    med, counts = _counter_medians(dirs)
     w = I.WORKLOADS[workload]
     esz = {"bf16": 2, "f32": 4, "fp8": 1}[w.dtype]
     gsz = 4 if w.dtype == "f32" else 2
-    algo = 2 * w.T * (w.hq + w.hk) * esz + ((2 * w.head_dim) if w.head_dim else (w.hq + w.hk)) * gsz
-    traffic = med["fetch"] * 1024.0 * f_scale + med["write"] * 1024.0 * w_scale
-    out = {
-        "workload": workload,
-        "kernel_source_hash": kernel_source_hash(),
-        "fetch_kib_per_dispatch": med["fetch"],
-        "write_kib_per_dispatch": med["write"],
-        "copy_known_bytes": copy_bytes,
-        "copy_fetch_kib": med["copy_fetch"],
-        "copy_write_kib": med["copy_write"],
-        "fetch_scale": f_scale,
-        "write_scale": w_scale,
-        "traffic_bytes_per_launch": traffic,
-        "algorithmic_bytes_per_launch": algo,
-        "traffic_over_algorithmic": traffic / algo,
-        "commands": commands,
+    h = w.hq + w.hk
+    span = w.T * h * esz
+    algo = {
+        "qknorm_fused": 2 * span + h * gsz,
+        "qknorm_headwise": 2 * span + 2 * w.head_dim * gsz,
+        "qknorm_partial_stats": span + 8 * w.T,
+        "qknorm_apply_with_stats": 2 * span + 8 * (1 + w.peers) * w.T + h * gsz,
+        "stream_copy": 2 * span,
+        "stream_read": span,
     }
+    kernels = {}
+    for call, m in sorted(med.items()):
+        b = request_bytes(m)
+        rec = {"dispatches": counts[call], "counters_median": m, **b}
+        if "read_bytes" in b and "write_bytes" in b:
+            rec["traffic_bytes_per_launch"] = b["read_bytes"] + b["write_bytes"]
+            rec["algorithmic_bytes_per_launch"] = algo.get(call)
+            if algo.get(call):
+                rec["traffic_over_algorithmic"] = rec["traffic_bytes_per_launch"] / algo[call]
+        kernels[call] = rec
+        log(f"[traffic] {call}: {json.dumps(rec)}")
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "kernels": kernels,
+           "formula": request_bytes.__doc__.split("\n\n")[0].replace("\n   ", ""), "commands": commands}
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -445,8 +639,8 @@ def shapes_table(dev, T=8192, steps=100):
         for hq, hk, hv in I.PREFILL_WIDTHS:
             w = replace(I.prefill_width(dtype, hq, hk, hv, T), head_dim=head_dim)
             step = FusedStep(w, I.make_inputs(w), dev, 1)
-            time_steps(step, 10, 300)
-            b2b = min(time_steps(step, steps, 20)[1] for _ in range(3)) / steps
+            time_steps(step, 10, 300, graph=False)
+            b2b = min(time_steps(step, steps, 20, graph=False)[1] for _ in range(3)) / steps
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
@@ -481,23 +675,34 @@ def shapes_table(dev, T=8192, steps=100):
     return rows
 
 
+def _plan_text(qk, w, call, shards):
+    if call == "qknorm_headwise":
+        return qk.describe_headwise_plan(w.hq, w.hk, w.T, w.head_dim, w.dtype, 0, ld=w.ld)
+    op = {"qknorm_fused": 0, "qknorm_partial_stats": 1, "qknorm_apply_with_stats": 2}[call]
+    return qk.describe_plan(op, w.hq, w.hk, w.T, w.dtype, shards if op == 0 else 1,
+                            ld=w.ld if w.packed else w.hq)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # Warm-up long enough (tens of ms at the prefill shapes) for clocks and
-    # the rotating buffers' first touches to settle before timing.
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="gqa_prefill")
     ap.add_argument("--shards", type=int, default=None, help="S for the fused workloads (default: first listed)")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's token count T (a size sweep; the default is the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
+    ap.add_argument("--ceiling-configs", default="",
+                    help="ceiling launches to sweep, as PERxBLOCK,... (default: all of CEIL_CONFIGS)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager calls from Python instead of one HIP-graph replay of the timed calls")
     ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="time a plain copy of this many bytes instead (calibration)")
-    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output (no GPU needed)")
-    ap.add_argument("--traffic-copy-bytes", type=int, default=100663296)
+                    help="time the streaming copy and read kernels on contiguous buffers of this many bytes")
+    ap.add_argument("--record-traffic", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output directories "
+                         "(no GPU needed)")
     ap.add_argument("--latency", action="store_true",
                     help="per-call times of the tiny, small-dense and decode workloads (one JSON line each)")
     ap.add_argument("--shapes", action="store_true",
@@ -506,12 +711,11 @@ def main():
     args = ap.parse_args()
 
     if args.record_traffic:
-        record_traffic(args.workload, *args.record_traffic, args.traffic_copy_bytes,
-                       [c for c in args.traffic_commands.split(";;") if c])
+        record_traffic(args.workload, args.record_traffic, [c for c in args.traffic_commands.split(";;") if c])
         return
 
     if args.gpus != 1:
-        print(f"bench.py: the kernels run on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path would shard by exchanging 2 float32 sums per token per rank, not implemented here)",
               file=sys.stderr)
         sys.exit(2)
@@ -537,12 +741,12 @@ def main():
         return
 
     if args.copy_bytes:
-        step = CopyStep(args.copy_bytes, dev)
-        wall, ev = time_steps(step, args.steps, args.warmup)
-        gbps = step.bytes / (ev / args.steps) / 1e9
-        print(json.dumps({"metric": "plain device copy", "bytes_per_launch": step.bytes,
-                          "ms_per_launch": ev / args.steps * 1e3, "GBps": gbps,
-                          "frac_of_peak": gbps / HBM_PEAK_GBPS, "steps": args.steps}), flush=True)
+        for copy in (True, False):
+            step = ContiguousCopy(args.copy_bytes, dev, copy)
+            rows, best = ceiling_sweep(step, dev, args.steps, args.warmup, graph=not args.eager)
+            print(json.dumps({"metric": f"streaming {'copy' if copy else 'read'} of a contiguous buffer",
+                              "buffer_bytes": step.n, "bytes_per_launch": step.bytes, "steps": args.steps,
+                              "rotating_sets": step.n_sets, "best": best, "sweep": rows}), flush=True)
         return
 
     w = I.WORKLOADS[args.workload]
@@ -556,35 +760,62 @@ def main():
     t0 = time.perf_counter()
     inp = I.make_inputs(w)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    if w.peers:
-        step = SplitStep(w, inp, dev)
-        plan = "; ".join(qk.describe_plan(op, w.hq, w.hk, w.T, w.dtype, 1, ld=w.ld) for op in (1, 2))
-    else:
-        step = FusedStep(w, inp, dev, shards)
-        if w.head_dim:
-            plan = qk.describe_headwise_plan(w.hq, w.hk, w.T, w.head_dim, w.dtype, 0, ld=w.ld)
-        else:
-            plan = qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld if w.packed else w.hq)
+    # One rank's slice runs the split path: Phase A, then Phase B with the
+    # received planes. Each call is timed alone over its own rotating sets.
+    steps = [PartialStep(w, inp, dev), ApplyStep(w, inp, dev)] if w.peers else [FusedStep(w, inp, dev, shards)]
     torch.cuda.synchronize()
-    log(f"[bench] plan: {plan}; {step.n_sets} rotating buffer sets, {step.footprint / 2**20:.0f} MiB")
+    plans = [_plan_text(qk, w, s.name, shards) for s in steps]
+    for s, plan in zip(steps, plans):
+        log(f"[bench] {s.name}: {plan}; {s.n_sets} rotating buffer sets, {s.footprint / 2**20:.0f} MiB")
 
-    wall, ev = time_steps(step, args.steps, args.warmup)
-    ms_per_step = wall / args.steps * 1e3
-    mean_launch_s = ev / args.steps
-    achieved = step.bytes / mean_launch_s / 1e9
-    log(f"[bench] {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms, "
-        f"{mean_launch_s * 1e6:.2f} us per step, {achieved:.0f} GB/s")
+    # The streaming ceilings of the same bytes, on the same buffers (before
+    # the timed calls: this also brings clocks and buffers to steady state).
+    ceilings = [None] * len(steps)
+    if not args.no_ceiling:
+        for n, s in enumerate(steps):
+            ceilings[n] = ceiling_sweep(s, dev, steps=max(args.steps, 100), warmup=100, graph=not args.eager,
+                                        configs=CEIL_CONFIGS if not args.ceiling_configs else
+                                        [tuple(int(v) for v in c.split("x")) for c in args.ceiling_configs.split(",")])
 
     khash = kernel_source_hash()
-    traffic = load_traffic(w.key, khash) if w.T == t_own else None  # counters were taken at the workload's T
+    kernels, wall_total = [], 0.0
+    for s, plan, ceil in zip(steps, plans, ceilings):
+        wall, ev = time_steps(s, args.steps, args.warmup, graph=not args.eager)
+        wall_total += wall
+        mean = ev / args.steps
+        achieved = s.bytes / mean / 1e9
+        log(f"[bench] {s.name}: {args.steps} calls, wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms, "
+            f"{mean * 1e6:.2f} us per call, {achieved:.0f} GB/s")
+        k = {
+            "kernel": s.name,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": load_traffic(w.key, s.name, khash) if w.T == t_own else None,
+            "algorithmic_bytes_per_launch": s.bytes,
+            "mean_launch_us": mean * 1e6,
+            "plan": plan,
+        }
+        if ceil is not None:
+            best = ceil[1]
+            # the ceiling moves the Q/K bytes only; compare rates of those bytes
+            rate = s.stream_bytes / mean / 1e9
+            k["ceiling"] = {"kernel": best["kernel"], "achieved": best["GBps"], "us": best["us"],
+                            "bytes": best["bytes"], "frac": best["frac_of_peak"]}
+            k["frac_of_ceiling"] = rate / best["GBps"]
+        k["kernel_source_hash"] = khash
+        kernels.append(k)
+    dominant = max(kernels, key=lambda k: k["mean_launch_us"])
     out = {
         "metric": "QK-Norm tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
-        "value": w.T * args.steps / wall,
+        "value": w.T * args.steps / wall_total,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall_total / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -597,24 +828,16 @@ def main():
             "hq": w.hq, "hk": w.hk, "hv": w.hv,
             "layout": f"packed [{w.T}, {w.ld}]" if w.packed else "separate Q/K arrays",
             "shards": shards,
-            "calls_per_step": step.name,
+            "calls_per_step": " + ".join(s.name for s in steps),
             "out_of_place": True,
-            "rotating_sets": step.n_sets,
-            "plan": plan,
+            "rotating_sets": [s.n_sets for s in steps],
+            "timing": "eager calls" if args.eager else "one HIP-graph replay of the timed calls",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_step": step.bytes,
-            "mean_step_us": mean_launch_s * 1e6,
-            "kernel_source_hash": khash,
-        },
+        "roofline": dominant,
         "cpu_baseline": None,
     }
+    if len(kernels) > 1:
+        out["roofline_kernels"] = kernels
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(w, inp)

@@ -62,9 +62,11 @@
  * stream's device; all pointers are device pointers that this device can
  * access. Calls on different streams or threads are independent; two calls
  * whose outputs overlap race, as any two kernels would. The kernels are
- * built for gfx950 only. The environment variable QKNORM_MAX_GRID (read at
- * each launch) caps the number of blocks per launch; blocks then loop over
- * several token groups. It exists for tests; results do not depend on it.
+ * built for gfx950 only. The environment variable QKNORM_MAX_GRID, read once
+ * when the library first launches a kernel, caps the number of blocks per
+ * launch (blocks then loop over several token groups), which leaves compute
+ * units to kernels running beside these on other streams; results do not
+ * depend on it.
  *
  * Errors
  * ------

@@ -143,6 +143,15 @@ def _rows(t, name):
     return st[0] if shape[0] > 1 else max(st[0], shape[1])
 
 
+def _same_device(t, ref, name):
+    """Every tensor a call hands to the library must be device memory of the
+    q tensor's GPU: a host pointer reaching a kernel faults the GPU."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.get_device() != ref.get_device():
+        raise ValueError(f"{name} is on device {t.get_device()}, q on device {ref.get_device()}")
+
+
 def _operand(x, y, gamma, name):
     op = Operand()
     op.ld_x = _rows(x, name)
@@ -153,6 +162,7 @@ def _operand(x, y, gamma, name):
         if y.shape != shape:
             raise ValueError(f"output for {name} has shape {tuple(y.shape)}, expected {tuple(shape)}")
         op.ld_y = _rows(y, "output for " + name)
+        _same_device(y, x, "output for " + name)
         if y.dtype != x.dtype:
             raise TypeError(f"output for {name} must have dtype {x.dtype}")
         op.y = y.data_ptr()
@@ -162,6 +172,7 @@ def _operand(x, y, gamma, name):
             raise ValueError(f"gamma for {name} must be contiguous [{shape[1]}]")
         if gamma.dtype != _gamma_dtype(x):
             raise TypeError(f"gamma for {name} must have dtype {_gamma_dtype(x)}")
+        _same_device(gamma, x, "gamma for " + name)
         op.gamma = gamma.data_ptr()
     return op
 
@@ -213,6 +224,7 @@ def qknorm_partial_stats(q, k, shards, partials=None, stream=None):
             or not partials.is_contiguous()):
         raise ValueError(f"partials must be contiguous float32 [{shards}, 2, {T}]")
     oq = _operand(q, None, None, "q")
+    _same_device(partials, q, "partials")
     ok = _operand(k, None, None, "k")
     _check(lib.qknorm_partial_stats(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), int(shards),
                                     partials.data_ptr(), _stream(q, stream)))
@@ -229,6 +241,8 @@ def qknorm_apply_with_stats(q, k, gamma_q, gamma_k, eps, stats, hq_full, hk_full
     if stats.dim() != 3 or stats.shape[1] != 2 or stats.shape[2] != T or stats.dtype != torch.float32 \
             or not stats.is_contiguous():
         raise ValueError(f"stats must be contiguous float32 [P, 2, {T}]")
+    _rows(q, "q")
+    _same_device(stats, q, "stats")
     out_q = q if out_q is None else out_q
     out_k = k if out_k is None else out_k
     oq = _operand(q, out_q, gamma_q, "q")
@@ -255,6 +269,7 @@ def qknorm_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, 
         need = (o.h // head_dim - 1) * gamma_head_stride + head_dim if head_dim > 0 else 0
         if g.dim() != 1 or g.shape[0] < need or (g.shape[0] > 1 and g.stride(0) != 1) or g.dtype != _gamma_dtype(q):
             raise ValueError(f"gamma for {name} must be contiguous, dtype {_gamma_dtype(q)}, >= {need} elements")
+        _same_device(g, q, "gamma for " + name)
         o.gamma = g.data_ptr()
     _check(lib.qknorm_headwise(ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), int(head_dim),
                                int(gamma_head_stride), _stream(q, stream)))

@@ -1,9 +1,11 @@
-"""Builds libqknorm.so in-tree with hipcc for gfx950.
+"""Builds libqknorm.so (the QK-Norm C ABI) and libstreamceil.so (the
+benchmark's streaming copy and read kernels) in-tree with hipcc for gfx950.
 
     python -m layerwise_qk_norm_qknorm_amd.build_lib
 
-Every build recompiles all sources. The library is written next to this file
-(``libqknorm.so``), where the binding loads it from.
+Every build recompiles all sources. The libraries are written next to this
+file, where the binding (``libqknorm.so``) and bench.py (``libstreamceil.so``)
+load them from.
 """
 
 import os
@@ -16,8 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm.so")
+CEIL_LIB = os.path.join(PKG, "libstreamceil.so")
 
 SOURCES = ["qknorm_api.cpp", "qknorm_kernels.hip"]
+CEIL_SOURCES = ["stream_ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -28,7 +32,7 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libqknorm.so)")
 
 
-def command(out):
+def command(out, sources=SOURCES):
     return [
         hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-function",
@@ -36,14 +40,14 @@ def command(out):
         # from plain float code, and they are not used anywhere here.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", CSRC,
-        *[os.path.join(CSRC, s) for s in SOURCES],
+        *[os.path.join(CSRC, s) for s in sources],
         "-o", out,
     ]
 
 
-def build(verbose=True):
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _build_one(lib, sources, verbose):
+    tmp = lib + ".tmp"
+    cmd = command(tmp, sources)
     if verbose:
         print("[build] " + " ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
@@ -53,8 +57,14 @@ def build(verbose=True):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=True):
+    """Compiles both libraries; returns the path of libqknorm.so."""
+    _build_one(CEIL_LIB, CEIL_SOURCES, verbose)
+    return _build_one(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -699,13 +699,18 @@ using HeadKernelFn = void (*)(const HeadArgs);
 
 constexpr int64_t kMaxGrid = (int64_t)1 << 30;
 
-// Largest grid a launch uses: kMaxGrid, or a smaller cap from the
-// QKNORM_MAX_GRID environment variable (read at each launch), under which
-// blocks loop over several token groups; tests use it to run that loop.
+// Largest grid a launch uses: kMaxGrid, or a smaller cap set by the
+// QKNORM_MAX_GRID environment variable when the library is first used (read
+// once per process), under which blocks loop over several token groups. A cap
+// leaves compute units free for kernels running beside these on other
+// streams; the tests use it to run the token loop.
 int64_t grid_cap() {
-  const char* e = std::getenv("QKNORM_MAX_GRID");
-  const long long v = e ? std::atoll(e) : 0;
-  return v > 0 && v < kMaxGrid ? (int64_t)v : kMaxGrid;
+  static const int64_t cap = [] {
+    const char* e = std::getenv("QKNORM_MAX_GRID");
+    const long long v = e ? std::atoll(e) : 0;
+    return v > 0 && v < kMaxGrid ? (int64_t)v : kMaxGrid;
+  }();
+  return cap;
 }
 
 template <class IO, int MODE, bool ALIGNED>

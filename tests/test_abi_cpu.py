@@ -224,6 +224,105 @@ def test_binding_refuses_cpu_tensors():
         qk.qknorm_fused(x[:, :32], x[:, 32:], g, g, 1e-6, 1)
 
 
+class FakeDevice:
+    """A CPU tensor posing as device memory of GPU `index` for the binding's
+    checks. Its data pointer is NULL, so anything that got past the binding
+    would be refused by the library's own argument check, never launched."""
+
+    def __init__(self, t, index=0):
+        self.t, self.index = t, index
+
+    shape = property(lambda self: self.t.shape)
+    dtype = property(lambda self: self.t.dtype)
+    is_cuda = True
+
+    def stride(self, *a):
+        return self.t.stride(*a)
+
+    def dim(self):
+        return self.t.dim()
+
+    def is_contiguous(self):
+        return self.t.is_contiguous()
+
+    def data_ptr(self):
+        return 0
+
+    def get_device(self):
+        return self.index
+
+    def __getitem__(self, idx):
+        return FakeDevice(self.t[idx], self.index)
+
+
+def _fake_case(dtype="bf16"):
+    import torch
+    td = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    x = FakeDevice(torch.zeros(4, 96, dtype=td))
+    g = FakeDevice(torch.ones(64, dtype=td))
+    return x, g, td
+
+
+@pytest.mark.parametrize("bad", ["gamma_cpu", "gamma_other_gpu", "out_cpu", "out_other_gpu"])
+def test_binding_refuses_host_or_foreign_operands(bad):
+    import torch
+    x, g, td = _fake_case()
+    q, k = x[:, :64], x[:, 64:]
+    gk = FakeDevice(torch.ones(32, dtype=td))
+    oq = FakeDevice(torch.zeros(4, 64, dtype=td))
+    gq = g
+    if bad == "gamma_cpu":
+        gq = torch.ones(64, dtype=td)
+    elif bad == "gamma_other_gpu":
+        gq = FakeDevice(torch.ones(64, dtype=td), index=1)
+    elif bad == "out_cpu":
+        oq = torch.zeros(4, 64, dtype=td)
+    else:
+        oq = FakeDevice(torch.zeros(4, 64, dtype=td), index=1)
+    with pytest.raises(ValueError):
+        qk.qknorm_fused(q, k, gq, gk, 1e-6, 1, oq, None)
+    with pytest.raises(ValueError):
+        qk.qknorm_apply_with_stats(q, k, gq, gk, 1e-6, FakeDevice(torch.zeros(1, 2, 4)), 64, 32, oq, None)
+
+
+def test_binding_refuses_host_statistics():
+    import torch
+    x, g, td = _fake_case()
+    q, k = x[:, :64], x[:, 64:]
+    gk = FakeDevice(torch.ones(32, dtype=td))
+    with pytest.raises(ValueError, match="partials"):
+        qk.qknorm_partial_stats(q, k, 1, torch.zeros(1, 2, 4))
+    with pytest.raises(ValueError, match="partials"):
+        qk.qknorm_partial_stats(q, k, 1, FakeDevice(torch.zeros(1, 2, 4), index=1))
+    with pytest.raises(ValueError, match="stats"):
+        qk.qknorm_apply_with_stats(q, k, g, gk, 1e-6, torch.zeros(1, 2, 4), 64, 32)
+    with pytest.raises(ValueError, match="stats"):
+        qk.qknorm_apply_with_stats(q, k, g, gk, 1e-6, FakeDevice(torch.zeros(2, 2, 4), index=1), 64, 32)
+
+
+@pytest.mark.parametrize("where", ["q", "k"])
+def test_binding_refuses_host_headwise_gamma(where):
+    import torch
+    x, _, td = _fake_case()
+    q, k = x[:, :64], x[:, 64:]
+    good = FakeDevice(torch.ones(32, dtype=td))
+    host = torch.ones(32, dtype=td)
+    gq, gk = (host, good) if where == "q" else (good, host)
+    with pytest.raises(ValueError, match="gamma"):
+        qk.qknorm_headwise(q, k, gq, gk, 1e-6, 32, 0)
+
+
+def test_binding_fake_device_reaches_library_check():
+    """The fake operands pass the binding when they are all on one GPU; the
+    library then refuses the NULL pointers itself (nothing is launched)."""
+    import torch
+    x, g, td = _fake_case()
+    gk = FakeDevice(torch.ones(32, dtype=td))
+    with pytest.raises(qk.QKNormError) as e:
+        qk.qknorm_fused(x[:, :64], x[:, 64:], g, gk, 1e-6, 1, stream=0)
+    assert e.value.status == INVALID
+
+
 def headwise(q, k, T=16, dtype=BF16, eps=1e-6, head_dim=64, stride=0):
     lib = qk.load_library()
     return lib.qknorm_headwise(ctypes.byref(q), ctypes.byref(k), T, dtype, eps, head_dim, stride, None)

@@ -4,9 +4,15 @@ loop many times (the LDS double buffer alternating, tokens past the end on
 the last pass). Results must equal, bit for bit, the same calls with one
 token group per block, for each layout: several waves per token, one-wave
 tokens four to a block, several tokens per wave, the split path and both
-headwise kernels."""
+headwise kernels.
+
+The library reads the cap once per process, so the capped calls run in one
+child process (tests/grid_cap_child.py) started with the variable set; this
+process makes the uncapped calls and compares."""
 
 import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -14,80 +20,52 @@ import torch
 
 import oracle
 import layerwise_qk_norm_qknorm_amd as qk
-from layerwise_qk_norm_qknorm_amd import inputs as I
-from gpu_helpers import DEV, check_bf16, np_to_torch, torch_to_np
+from gpu_helpers import check_bf16
+from grid_cases import HEAD_CASES, ROW_CASES, row_inputs, run_head_case, run_row_case
 
 pytestmark = pytest.mark.gpu
 
+CAP = 7   # far fewer blocks than token groups
+HERE = os.path.dirname(os.path.abspath(__file__))
 
-@pytest.fixture(scope="module", autouse=True)
-def _gpu():
+
+@pytest.fixture(scope="module")
+def capped(tmp_path_factory):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    assert "QKNORM_MAX_GRID" not in os.environ, "the uncapped calls need the variable unset"
     qk.load_library()
-    yield
-    os.environ.pop("QKNORM_MAX_GRID", None)
-    torch.cuda.synchronize()
+    out = str(tmp_path_factory.mktemp("gridcap") / "capped.npz")
+    env = dict(os.environ, QKNORM_MAX_GRID=str(CAP))
+    print(f"[case] grid loop: child process with QKNORM_MAX_GRID={CAP}", flush=True)
+    res = subprocess.run([sys.executable, "-u", os.path.join(HERE, "grid_cap_child.py"), out], env=env,
+                         capture_output=True, text=True, timeout=300)
+    print(res.stdout[-2000:], res.stderr[-2000:], flush=True)
+    assert res.returncode == 0, f"child process failed ({res.returncode})"
+    with np.load(out) as d:
+        return {k: d[k] for k in d.files}
 
 
-def _run(cap, fn):
-    if cap:
-        os.environ["QKNORM_MAX_GRID"] = str(cap)
-    try:
-        out = fn()
-        torch.cuda.synchronize()
-    finally:
-        os.environ.pop("QKNORM_MAX_GRID", None)
-    return [torch_to_np(o) for o in out]
-
-
-@pytest.mark.parametrize("T,hq,hk,dtype,shards", [
-    (1031, 5120, 1024, "bf16", 1),     # 4 waves per token, LDS exchange
-    (1029, 1280, 256, "bf16", 1),      # one-wave tokens, four to a block
-    (1500, 640, 128, "bf16", 1),       # 32 lanes per token, 8 tokens per block
-    (999, 2048, 512, "fp8", 4),        # FP8, four shards in one wave (few tokens: one slot)
-    (777, 1024, 256, "f32", 2),        # fp32, two shards over two waves
-])
-def test_looping_blocks_equal_one_group_per_block(T, hq, hk, dtype, shards):
-    inp = I.make_custom(T, hq, hk, 0, dtype, seed=T + hq)
-    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
-    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
-
-    def calls():
-        fq, fk = torch.empty_like(xq), torch.empty_like(xk)
-        qk.qknorm_fused(xq, xk, gq, gk, 1e-6, shards, fq, fk)
-        part = qk.qknorm_partial_stats(xq, xk, shards)
-        aq, ak = torch.empty_like(xq), torch.empty_like(xk)
-        qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, part, hq, hk, aq, ak)
-        return fq, fk, part, aq, ak
-
+@pytest.mark.parametrize("case", ROW_CASES, ids=lambda c: "_".join(map(str, c)))
+def test_looping_blocks_equal_one_group_per_block(case, capped):
+    T, hq, hk, dtype, shards = case
     plan = qk.describe_plan(0, hq, hk, T, dtype, shards)
     tpb = int(plan.split("tokens/block=")[1].split()[0])
-    cap = 7                                   # far fewer blocks than token groups
-    assert -(-T // tpb) > 20 * cap
-    print(f"[case] grid loop T={T} {dtype} S={shards} plan: {plan}; cap {cap}", flush=True)
-    base = _run(0, calls)
-    looped = _run(cap, calls)
-    for a, b in zip(base, looped):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert -(-T // tpb) > 20 * CAP
+    print(f"[case] grid loop T={T} {dtype} S={shards} plan: {plan}; cap {CAP}", flush=True)
+    base = run_row_case(*case)
+    for n, a in enumerate(base):
+        assert np.array_equal(a.view(np.uint8), capped[f"rows_{'_'.join(map(str, case))}_{n}"])
     if dtype == "bf16":
+        inp = row_inputs(T, hq, hk, dtype)
         ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, dtype, 1e-6, shards)
-        check_bf16(looped[0], ref.yq_bits, "looped Q")
+        looped_q = capped[f"rows_{'_'.join(map(str, case))}_0"].view(np.uint16).reshape(T, hq)
+        check_bf16(looped_q, ref.yq_bits, "looped Q")
 
 
-@pytest.mark.parametrize("head_dim", [128, 72])    # token-wide and per-head kernels
-def test_looping_blocks_headwise(head_dim):
-    T, hq, hk = 1201, 16 * head_dim, 4 * head_dim
-    inp = I.make_custom(T, hq, hk, 0, "bf16", seed=77 + head_dim)
-    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
-    gq, gk = np_to_torch(inp.gamma_q[:head_dim].copy()).to(DEV), np_to_torch(inp.gamma_k[:head_dim].copy()).to(DEV)
-
-    def calls():
-        oq, ok = torch.empty_like(xq), torch.empty_like(xk)
-        qk.qknorm_headwise(xq, xk, gq, gk, 1e-6, head_dim, 0, oq, ok)
-        return oq, ok
-
-    base = _run(0, calls)
-    looped = _run(5, calls)
-    for a, b in zip(base, looped):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+@pytest.mark.parametrize("head_dim", HEAD_CASES)
+def test_looping_blocks_headwise(head_dim, capped):
+    print(f"[case] grid loop headwise head_dim={head_dim}; cap {CAP}", flush=True)
+    base = run_head_case(head_dim)
+    for n, a in enumerate(base):
+        assert np.array_equal(a.view(np.uint8), capped[f"heads_{head_dim}_{n}"])
