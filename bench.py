@@ -472,14 +472,19 @@ def _counter_medians(dirs):
 
 
 def request_bytes(m):
-    """Bytes the L2 requested from the fabric, from the request counters:
-    reads are 128-, 64- or 32-byte requests (TCC_BUBBLE counts the 128-byte
-    ones, TCC_EA0_RDREQ_32B the 32-byte ones, TCC_EA0_RDREQ all), writes 64-
-    or 32-byte requests (TCC_EA0_WRREQ_64B the 64-byte ones)."""
+    """Bytes the L2 requested from the fabric, from the request counters.
+    Reads: 128 bytes per TCC_EA0_RDREQ that is not a 32-byte one
+    (TCC_EA0_RDREQ_32B). On MI355X with ROCm 7 these requests are whole
+    128-byte lines, but TCC_BUBBLE (the counter of 128-byte read requests,
+    which rocprofv3's FETCH_SIZE expression relies on) reads 0, so FETCH_SIZE
+    counts them as 64 bytes, half the bytes moved. Writes: 64 bytes per
+    TCC_EA0_WRREQ_64B and 32 per other TCC_EA0_WRREQ (the WRITE_SIZE
+    expression). record_traffic checks both against the streaming copy or
+    read of a known byte count profiled in the same runs."""
     out = {}
     if "TCC_EA0_RDREQ_sum" in m:
-        rd, r32, r128 = m["TCC_EA0_RDREQ_sum"], m.get("TCC_EA0_RDREQ_32B_sum", 0.0), m.get("TCC_BUBBLE_sum", 0.0)
-        out["read_bytes"] = 128.0 * r128 + 64.0 * (rd - r128 - r32) + 32.0 * r32
+        rd, r32 = m["TCC_EA0_RDREQ_sum"], m.get("TCC_EA0_RDREQ_32B_sum", 0.0)
+        out["read_bytes"] = 128.0 * (rd - r32) + 32.0 * r32
     if "TCC_EA0_WRREQ_sum" in m:
         wr, w64 = m["TCC_EA0_WRREQ_sum"], m.get("TCC_EA0_WRREQ_64B_sum", 0.0)
         out["write_bytes"] = 64.0 * w64 + 32.0 * (wr - w64)
@@ -517,8 +522,16 @@ def record_traffic(workload, dirs, commands):
                 rec["traffic_over_algorithmic"] = rec["traffic_bytes_per_launch"] / algo[call]
         kernels[call] = rec
         log(f"[traffic] {call}: {json.dumps(rec)}")
+    # The streaming kernels move a known byte count: the formula must give it.
+    for call, known_read, known_write in (("stream_copy", span, span), ("stream_read", span, 0)):
+        k = kernels.get(call)
+        if k and "read_bytes" in k and "write_bytes" in k:
+            for got, want in ((k["read_bytes"], known_read), (k["write_bytes"], known_write)):
+                if abs(got - want) > 0.005 * max(want, 1):
+                    raise SystemExit(f"[traffic] {call}: counters give {got} bytes, {want} known: formula does not hold")
+            k["check"] = "read and write bytes within 0.5% of the known bytes"
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "kernels": kernels,
-           "formula": request_bytes.__doc__.split("\n\n")[0].replace("\n   ", ""), "commands": commands}
+           "formula": " ".join(request_bytes.__doc__.split()), "commands": commands}
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

@@ -456,12 +456,13 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
     if (few_tokens) {
       score = (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac + (waves > 8 ? 1.5 : 0.0) -
               0.01 * waves;
-    } else if (dtype == kDtypeBF16 && T < 8192) {
-      // Mid-size bf16 launches (1024 to 8191 tokens) run best over fewer
-      // waves with 3 to 6 chunks per lane, whether their rows stream from
-      // HBM or sit in the last-level cache (timed with and without rotating
-      // buffers at T = 512 to 4096: 1.8% from the fastest layout on average,
-      // against 3.6% and 11% for the rule below).
+    } else if (dtype == kDtypeBF16 && mode == MODE_FUSED && T <= 4096) {
+      // Mid-size fused bf16 launches (1024 to 4096 tokens, the range timed)
+      // run best over fewer waves with 3 to 6 chunks per lane, whether their
+      // rows stream from HBM or sit in the last-level cache (timed with and
+      // without rotating buffers at T = 512 to 4096: 1.8% from the fastest
+      // layout on average, against 3.6% and 11% for the rule below). Larger
+      // launches and the split calls keep the prefill rule.
       score = (v == 3 || v == 4 ? 0.0 : v == 6 ? 0.1 : v == 2 ? 0.3 : v == 8 ? 0.4 : v == 1 ? 10.0 : 1.0) +
               (wfrac > 0.25 ? 8.0 : 2.0 * wfrac) + (waves > 4 ? 0.3 : 0.0) + (waves >= 13 ? 3.0 : 0.0) +
               0.01 * waves;

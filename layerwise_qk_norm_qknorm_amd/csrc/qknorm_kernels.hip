@@ -213,14 +213,36 @@ __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chu
   }
 }
 
-// Sum of squares of one chunk, in element order (Phase A, in-lane part).
-template <class IO>
+// Sum of squares of one chunk (Phase A, in-lane part). bf16 rows: the
+// gfx950 two-way bf16 dot product with a float32 accumulator, two squares per
+// instruction straight from the packed words (products exact, denormal
+// products kept). FP8 rows with DOT: each pair of E4M3 values is first widened
+// exactly to a bf16 pair, then the same dot product; without DOT (where the
+// kernel widens the chunk to float32 for the scaling anyway and keeps it) a
+// chain of fused multiply-adds on the float32 values, like fp32 rows.
+template <class IO, bool DOT = true>
 __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
-  float v[IO::kVW];
-  decode<IO>(c, v);
   float s = 0.0f;
+  if constexpr (IO::kDtype == kDtypeBF16) {
 #pragma unroll
-  for (int e = 0; e < IO::kVW; ++e) s = __builtin_fmaf(v[e], v[e], s);
+    for (int p = 0; p < 4; ++p) {
+      const bf16x2_t w = __builtin_bit_cast(bf16x2_t, c.w[p]);
+      s = __builtin_amdgcn_fdot2_f32_bf16(w, w, s, false);
+    }
+  } else if constexpr (IO::kDtype == kDtypeFP8 && DOT) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.w[p], 1.0f, false);
+      const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.w[p], 1.0f, true);
+      s = __builtin_amdgcn_fdot2_f32_bf16(lo, lo, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(hi, hi, s, false);
+    }
+  } else {
+    float v[IO::kVW];
+    decode<IO>(c, v);
+#pragma unroll
+    for (int e = 0; e < IO::kVW; ++e) s = __builtin_fmaf(v[e], v[e], s);
+  }
   return s;
 }
 
@@ -373,7 +395,11 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <class IO, int V, int MODE, bool ALIGNED>
+// WW (whole waves): one shard, and a token spans whole waves (several tokens
+// to a block only at one wave each), so the token index and all row
+// arithmetic are wave-uniform and run on the scalar unit; the general form
+// (WW false) also holds several shards and tokens that share a wave.
+template <class IO, int V, int MODE, bool ALIGNED, bool WW>
 __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_rows(const RowArgs a) {
   extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token] float2 (Q, K)
   constexpr int VW = IO::kVW;
@@ -384,11 +410,12 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   // wave (64 lanes, or 4..32 so that several tokens share a wave), and shards
   // share a token only with power-of-two lane groups, so the lane
   // decomposition is shifts and masks.
-  const int j = a.tokens_per_block > 1 ? tid >> a.log2_tok : 0;   // token slot within the block
-  const int r = a.tokens_per_block > 1 ? tid & (G - 1) : tid;     // thread within the token
-  const int s = a.shards > 1 ? r >> a.log2_lanes : 0;     // shard group
-  const int m = a.shards > 1 ? r & (L - 1) : r;           // lane within the group
-  const int qbase = __umul24(s, a.hq_s), kbase = __umul24(s, a.hk_s);
+  const int j = WW ? (a.tokens_per_block > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0)
+                   : (a.tokens_per_block > 1 ? tid >> a.log2_tok : 0);      // token slot within the block
+  const int r = WW ? tid - (j << 6) : a.tokens_per_block > 1 ? tid & (G - 1) : tid;  // thread within the token
+  const int s = !WW && a.shards > 1 ? r >> a.log2_lanes : 0;     // shard group
+  const int m = !WW && a.shards > 1 ? r & (L - 1) : r;           // lane within the group
+  const int qbase = WW ? 0 : __umul24(s, a.hq_s), kbase = WW ? 0 : __umul24(s, a.hk_s);
 
   // Token-invariant geometry of this lane's chunk slots.
   bool isq[V];
@@ -421,9 +448,21 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   const int64_t step = (int64_t)gridDim.x * tpb;
   int buf = 0;
 
+  // Token groups follow blockIdx, except for partial_stats: there each run of
+  // 64 blocks is transposed as 8 x 8, so that the 8 blocks the hardware
+  // places on one XCD (block i goes to XCD i mod 8) take 8 consecutive token
+  // groups, whose sums share cache lines of the partials, and a line is
+  // written from one L2 (measured 2-3% faster; the calls that also write rows
+  // were not faster). Each block still covers every gridDim-th group after its
+  // first, so every group is covered once.
+  int64_t g0 = blockIdx.x;
+  if (MODE == MODE_STATS && (int64_t)blockIdx.x < ((int64_t)gridDim.x & ~(int64_t)63)) {
+    const int r64 = blockIdx.x & 63;
+    g0 = ((int64_t)blockIdx.x & ~(int64_t)63) | ((r64 & 7) << 3) | (r64 >> 3);
+  }
   // The loop bound is uniform over the block (barriers inside); a token slot
   // past the end reads a valid row and writes nothing.
-  for (int64_t tb = (int64_t)blockIdx.x * tpb; tb < a.T; tb += step) {
+  for (int64_t tb = g0 * tpb; tb < a.T; tb += step) {
     const int64_t t = tb + j;
     const bool active = t < a.T;
     const int64_t tr = active ? t : a.T - 1;
@@ -444,7 +483,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       float aq = 0.0f, ak = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const float cs = cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
+        // FP8 rows of at most 4 slots keep the float32 widening for the
+        // scaling, so their sums reuse it; elsewhere the dot products.
+        constexpr bool kDot = !(IO::kDtype == kDtypeFP8 && MODE != MODE_STATS && V <= 4);
+        const float cs = cnt[i] > 0 ? chunk_sumsq<IO, kDot>(xv[i]) : 0.0f;
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
@@ -465,7 +507,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         } else {
           ssq = lane_read(aq, 0);
           ssk = lane_read(ak, 0);
-          for (int sh = 1; sh < a.shards; ++sh) {
+          for (int sh = 1; sh < (WW ? 1 : a.shards); ++sh) {
             ssq += lane_read(aq, sh * L);
             ssk += lane_read(ak, sh * L);
           }
@@ -482,7 +524,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         const int lane = tid & 63;
         const float2 pv = rb[lane < gpt ? lane : 0];
         float mq = 0.0f, mk = 0.0f;  // partial_stats: the sums of shard r
-        for (int sh = 0, q0 = 0; sh < a.shards; ++sh, q0 += gps) {
+        for (int sh = 0, q0 = 0; sh < (WW ? 1 : a.shards); ++sh, q0 += gps) {
           float pq = lane_read(pv.x, q0), pk = lane_read(pv.y, q0);
           for (int q = 1; q < gps; ++q) {
             pq += lane_read(pv.x, q0 + q);
@@ -596,7 +638,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f;
+    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO, !(IO::kDtype == kDtypeFP8 && V <= 4)>(xv[i]) : 0.0f;
     acc = group_sum(acc, L);
 
     {
@@ -677,7 +719,8 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float ss[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO>(xv[i]) : 0.0f, nc);
+    for (int i = 0; i < V; ++i)
+      ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO, !(IO::kDtype == kDtypeFP8 && V <= 4)>(xv[i]) : 0.0f, nc);
 
     {
       if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
@@ -713,34 +756,40 @@ int64_t grid_cap() {
   return cap;
 }
 
-template <class IO, int MODE, bool ALIGNED>
+template <class IO, int MODE, bool ALIGNED, bool WW>
 KernelFn pick_slots(int v) {
   switch (v) {
-    case 1: return qknorm_rows<IO, 1, MODE, ALIGNED>;
-    case 2: return qknorm_rows<IO, 2, MODE, ALIGNED>;
-    case 3: return qknorm_rows<IO, 3, MODE, ALIGNED>;
-    case 4: return qknorm_rows<IO, 4, MODE, ALIGNED>;
-    case 6: return qknorm_rows<IO, 6, MODE, ALIGNED>;
-    case 8: return qknorm_rows<IO, 8, MODE, ALIGNED>;
+    case 1: return qknorm_rows<IO, 1, MODE, ALIGNED, WW>;
+    case 2: return qknorm_rows<IO, 2, MODE, ALIGNED, WW>;
+    case 3: return qknorm_rows<IO, 3, MODE, ALIGNED, WW>;
+    case 4: return qknorm_rows<IO, 4, MODE, ALIGNED, WW>;
+    case 6: return qknorm_rows<IO, 6, MODE, ALIGNED, WW>;
+    case 8: return qknorm_rows<IO, 8, MODE, ALIGNED, WW>;
   }
   if constexpr (max_slots(IO::kDtype, ALIGNED) == kMaxSlots) {
-    if (v == 12) return qknorm_rows<IO, 12, MODE, ALIGNED>;
-    if (v == 16) return qknorm_rows<IO, 16, MODE, ALIGNED>;
+    if (v == 12) return qknorm_rows<IO, 12, MODE, ALIGNED, WW>;
+    if (v == 16) return qknorm_rows<IO, 16, MODE, ALIGNED, WW>;
   }
   return nullptr;
 }
 
+// The scalar-token form serves partial_stats on the 16-byte path only; the
+// element-wise path is the general kernel.
 template <class IO, int MODE>
-KernelFn pick_aligned(bool aligned, int v) {
-  return aligned ? pick_slots<IO, MODE, true>(v) : pick_slots<IO, MODE, false>(v);
+KernelFn pick_aligned(bool aligned, bool ww, int v) {
+  if (!aligned) return pick_slots<IO, MODE, false, false>(v);
+  if constexpr (MODE == MODE_STATS) {
+    if (ww) return pick_slots<IO, MODE, true, true>(v);
+  }
+  return pick_slots<IO, MODE, true, false>(v);
 }
 
 template <class IO>
-KernelFn pick_mode(int mode, bool aligned, int v) {
+KernelFn pick_mode(int mode, bool aligned, bool ww, int v) {
   switch (mode) {
-    case MODE_FUSED: return pick_aligned<IO, MODE_FUSED>(aligned, v);
-    case MODE_STATS: return pick_aligned<IO, MODE_STATS>(aligned, v);
-    case MODE_APPLY: return pick_aligned<IO, MODE_APPLY>(aligned, v);
+    case MODE_FUSED: return pick_aligned<IO, MODE_FUSED>(aligned, ww, v);
+    case MODE_STATS: return pick_aligned<IO, MODE_STATS>(aligned, ww, v);
+    case MODE_APPLY: return pick_aligned<IO, MODE_APPLY>(aligned, ww, v);
   }
   return nullptr;
 }
@@ -781,10 +830,16 @@ HeadKernelFn pick_head_kernel(const Plan& p) {
 }
 
 KernelFn pick_kernel(const Plan& p) {
+  // partial_stats with one shard and whole waves per token (several tokens to
+  // a block only at one wave each) takes the scalar-token form (measured 3.5%
+  // faster on the rank slice; the calls that also scale and store were not
+  // faster with it)
+  const bool ww = p.mode == MODE_STATS && p.shards == 1 && p.tok_threads % 64 == 0 &&
+                  (p.tokens_per_block == 1 || p.tok_threads == 64);
   switch (p.dtype) {
-    case kDtypeBF16: return pick_mode<BF16>(p.mode, p.aligned, p.slots);
-    case kDtypeF32: return pick_mode<F32>(p.mode, p.aligned, p.slots);
-    case kDtypeFP8: return pick_mode<FP8>(p.mode, p.aligned, p.slots);
+    case kDtypeBF16: return pick_mode<BF16>(p.mode, p.aligned, ww, p.slots);
+    case kDtypeF32: return pick_mode<F32>(p.mode, p.aligned, ww, p.slots);
+    case kDtypeFP8: return pick_mode<FP8>(p.mode, p.aligned, ww, p.slots);
   }
   return nullptr;
 }

@@ -158,6 +158,21 @@ def test_prefill_plans_are_the_measured_best(dtype):
         assert (int(f["lanes/shard"]), int(f["slots"])) == (lanes, slots), (dtype, hq, hk, f)
 
 
+# A mid-size fused bf16 launch (T = 1536, rows 4096/4096): the mid-size rule's
+# 256 lanes x 4 chunks; the prefill rule's 384 x 3 timed 12 to 32% slower on
+# MI355X for these rows (the worst case of that rule at mid sizes). The split calls and launches above 4096
+# tokens keep the prefill rule (only fused launches of 1024 to 4096 tokens
+# were timed for the mid-size rule).
+def test_mid_size_fused_bf16_plan():
+    f = fields(qk.describe_plan(0, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
+    assert (int(f["lanes/shard"]), int(f["slots"])) == (256, 4), f
+    for op in (1, 2):
+        g = fields(qk.describe_plan(op, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
+        assert (int(g["lanes/shard"]), int(g["slots"])) == (384, 3), (op, g)
+    h = fields(qk.describe_plan(0, 4096, 4096, 6144, "bf16", 1, ld=3 * 4096))
+    assert (int(h["lanes/shard"]), int(h["slots"])) == (384, 3), h
+
+
 def prefill_candidates(nc, dtype):
     """(lanes, slots, waves, idle fraction) of every feasible one-shard layout
     of a prefill launch (T >= 1024) on the 16-byte path."""
