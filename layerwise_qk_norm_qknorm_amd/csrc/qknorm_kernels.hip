@@ -490,9 +490,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
-      // Across the lanes of a group: every lane ends with the group's sum.
-      aq = group_sum(aq, group);
-      ak = group_sum(ak, group);
+      // Across the lanes of a group: every lane ends with the group's sum
+      // (one shard over whole waves: always 64-lane groups).
+      aq = WW ? group_sum_of<64>(aq) : group_sum(aq, group);
+      ak = WW ? group_sum_of<64>(ak) : group_sum(ak, group);
       if (G <= 64) {
         // One wave per token: group s is shard s; its sum sits in lane s*L.
         // Several tokens per wave (one shard each): the group is the token.
