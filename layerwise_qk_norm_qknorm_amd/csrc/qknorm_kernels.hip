@@ -213,17 +213,17 @@ __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chu
   }
 }
 
-// Sum of squares of one chunk (Phase A, in-lane part). bf16 rows: the
-// gfx950 two-way bf16 dot product with a float32 accumulator, two squares per
-// instruction straight from the packed words (products exact, denormal
-// products kept). FP8 rows with DOT: each pair of E4M3 values is first widened
-// exactly to a bf16 pair, then the same dot product; without DOT (where the
-// kernel widens the chunk to float32 for the scaling anyway and keeps it) a
-// chain of fused multiply-adds on the float32 values, like fp32 rows.
-template <class IO, bool DOT = true>
+// Sum of squares of one chunk (Phase A, in-lane part). With DOT, bf16 rows
+// use the gfx950 two-way bf16 dot product with a float32 accumulator, two
+// squares per instruction straight from the packed words (products exact,
+// denormal products kept), and FP8 rows first widen each pair of E4M3 values
+// exactly to a bf16 pair for the same dot product. Without DOT (where the
+// kernel widens the chunk to float32 for the scaling anyway and keeps it) and
+// for fp32 rows: a chain of fused multiply-adds in element order.
+template <class IO, bool DOT>
 __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
   float s = 0.0f;
-  if constexpr (IO::kDtype == kDtypeBF16) {
+  if constexpr (IO::kDtype == kDtypeBF16 && DOT) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const bf16x2_t w = __builtin_bit_cast(bf16x2_t, c.w[p]);
@@ -244,6 +244,16 @@ __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
     for (int e = 0; e < IO::kVW; ++e) s = __builtin_fmaf(v[e], v[e], s);
   }
   return s;
+}
+
+// Whether a kernel with V chunk slots that also scales (SCALES) takes the dot
+// product sums: packed rows held in up to 2 (bf16) or 4 (FP8) slots stay
+// widened to float32 from the sums to the scaling, so their sums reuse that
+// widening (measured faster there); above that, and for partial_stats, the
+// rows are widened again for the scaling and the dot products save the work.
+template <class IO, int V, bool SCALES>
+constexpr bool sums_by_dot() {
+  return IO::kBytes < 4 && !(SCALES && V <= (IO::kBytes == 2 ? 2 : 4));
 }
 
 // Largest magnitude of N values (NaN if any is NaN): one three-operand
@@ -483,10 +493,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       float aq = 0.0f, ak = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        // FP8 rows of at most 4 slots keep the float32 widening for the
-        // scaling, so their sums reuse it; elsewhere the dot products.
-        constexpr bool kDot = !(IO::kDtype == kDtypeFP8 && MODE != MODE_STATS && V <= 4);
-        const float cs = cnt[i] > 0 ? chunk_sumsq<IO, kDot>(xv[i]) : 0.0f;
+        const float cs = cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, MODE != MODE_STATS>()>(xv[i]) : 0.0f;
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
@@ -639,7 +646,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO, !(IO::kDtype == kDtypeFP8 && V <= 4)>(xv[i]) : 0.0f;
+    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, true>()>(xv[i]) : 0.0f;
     acc = group_sum(acc, L);
 
     {
@@ -721,7 +728,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     float ss[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
-      ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO, !(IO::kDtype == kDtypeFP8 && V <= 4)>(xv[i]) : 0.0f, nc);
+      ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, true>()>(xv[i]) : 0.0f, nc);
 
     {
       if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
