@@ -781,12 +781,12 @@ KernelFn pick_slots(int v) {
   return nullptr;
 }
 
-// The scalar-token form serves partial_stats on the 16-byte path only; the
-// element-wise path is the general kernel.
+// The scalar-token form serves partial_stats and fused FP8 rows on the
+// 16-byte path only; the element-wise path is the general kernel.
 template <class IO, int MODE>
 KernelFn pick_aligned(bool aligned, bool ww, int v) {
   if (!aligned) return pick_slots<IO, MODE, false, false>(v);
-  if constexpr (MODE == MODE_STATS) {
+  if constexpr (MODE == MODE_STATS || (MODE == MODE_FUSED && IO::kDtype == kDtypeFP8)) {
     if (ww) return pick_slots<IO, MODE, true, true>(v);
   }
   return pick_slots<IO, MODE, true, false>(v);
@@ -838,12 +838,13 @@ HeadKernelFn pick_head_kernel(const Plan& p) {
 }
 
 KernelFn pick_kernel(const Plan& p) {
-  // partial_stats with one shard and whole waves per token (several tokens to
-  // a block only at one wave each) takes the scalar-token form (measured 3.5%
-  // faster on the rank slice; the calls that also scale and store were not
-  // faster with it)
-  const bool ww = p.mode == MODE_STATS && p.shards == 1 && p.tok_threads % 64 == 0 &&
-                  (p.tokens_per_block == 1 || p.tok_threads == 64);
+  // One shard and whole waves per token (several tokens to a block only at
+  // one wave each): partial_stats and fused FP8 rows take the scalar-token
+  // form (measured 3.5% faster on the rank slice and 2% on the FP8 GQA
+  // prefill; fused bf16 rows and apply_with_stats were not faster with it:
+  // they are memory-bound and the scalar row arithmetic adds latency).
+  const bool ww = (p.mode == MODE_STATS || (p.mode == MODE_FUSED && p.dtype == kDtypeFP8)) && p.shards == 1 &&
+                  p.tok_threads % 64 == 0 && (p.tokens_per_block == 1 || p.tok_threads == 64);
   switch (p.dtype) {
     case kDtypeBF16: return pick_mode<BF16>(p.mode, p.aligned, ww, p.slots);
     case kDtypeF32: return pick_mode<F32>(p.mode, p.aligned, ww, p.slots);
