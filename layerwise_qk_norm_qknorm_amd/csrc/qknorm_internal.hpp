@@ -97,6 +97,7 @@ struct RowArgs {
   float* partials;    // MODE_STATS: [S][2][T]
   const float* stats; // MODE_APPLY: [P][2][T]
   int n_planes;
+  int stagger;        // 1: the first resident generation of blocks starts staggered (large launches)
 };
 
 // Headwise kernel arguments: every head of head_dim columns is normalized on

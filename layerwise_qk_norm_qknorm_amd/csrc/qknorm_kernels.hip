@@ -465,6 +465,17 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   // written from one L2 (measured 2-3% faster; the calls that also write rows
   // were not faster). Each block still covers every gridDim-th group after its
   // first, so every group is covered once.
+  // Large fused and apply launches: the blocks of the first resident
+  // generation start at 8 staggered times, 128 clocks apart (groups of 8
+  // consecutive blocks, one per XCD). Started together, that generation's
+  // reads are served interleaved and its blocks all finish at once, and the
+  // burst of scaling work then delays the next generation's loads. Staggered,
+  // apply launches ran 1.6% faster (bf16 and FP8 rows), fused FP8 rows about
+  // as much, fused bf16 rows unchanged.
+  if (MODE != MODE_STATS && a.stagger && blockIdx.x < 2048) {
+    const int k = (blockIdx.x >> 3) & 7;
+    for (int q = 0; q < k; ++q) __builtin_amdgcn_s_sleep(2);
+  }
   int64_t g0 = blockIdx.x;
   if (MODE == MODE_STATS && (int64_t)blockIdx.x < ((int64_t)gridDim.x & ~(int64_t)63)) {
     const int r64 = blockIdx.x & 63;
@@ -869,6 +880,7 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   // hipLaunchKernel returns this launch's own status (no sticky error from
   // an earlier, unrelated call is reported as ours).
   RowArgs a = args;
+  a.stagger = grid >= 4096 ? 1 : 0;  // only launches of at least two resident generations
   void* kargs[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
                                        dim3((unsigned)p.threads), kargs, (size_t)p.lds_bytes,
