@@ -131,14 +131,19 @@ __device__ __forceinline__ void pack<F32>(Chunk& c, const float (&v)[4]) {
   for (int p = 0; p < 4; ++p) c.w[p] = __float_as_uint(v[p]);
 }
 __device__ __forceinline__ float sat_e4m3(float x) { return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x); }
+// Four float32 values -> four E4M3 codes in one word, each conversion
+// filling one 16-bit half. The first one's word operand (the half it keeps)
+// is its own first input, dead afterwards, instead of a zeroed register: the
+// second conversion overwrites that half anyway, and no move is needed.
+__device__ __forceinline__ uint32_t pack_fp8_word(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 template <>
 __device__ __forceinline__ void pack<FP8>(Chunk& c, const float (&v)[16]) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * p], v[4 * p + 1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * p + 2], v[4 * p + 3], w, true);
-    c.w[p] = (uint32_t)w;
-  }
+  for (int p = 0; p < 4; ++p) c.w[p] = pack_fp8_word(v[4 * p], v[4 * p + 1], v[4 * p + 2], v[4 * p + 3]);
 }
 
 // Loads `W` words at `p`: 16-byte loads (p 16-byte aligned) on the aligned
@@ -256,53 +261,60 @@ constexpr bool sums_by_dot() {
   return IO::kBytes < 4 && !(SCALES && V <= (IO::kBytes == 2 ? 2 : 4));
 }
 
-// Largest magnitude of N values (NaN if any is NaN): one three-operand
-// maximum per two elements.
-template <int N>
-__device__ __forceinline__ float max_abs(const float (&v)[N]) {
-  float m = __builtin_fabsf(v[0]);
-#pragma unroll
-  for (int e = 1; e + 1 < N; e += 2)
-    m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(v[e])), __builtin_fabsf(v[e + 1]));
-  if (N % 2 == 0) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[N - 1]));
-  return m;
-}
-
 // Phase B and the final scaling for this lane's chunks of one token:
 // y = (x * gamma) * r[i], one rounding to the I/O type, stores of the valid
 // chunks (slot i goes to the Q or the K row). For FP8 the saturating
-// conversion costs four operations per element, so with up to 4 slots the
-// wave first checks whether any result exceeds 448 in magnitude or is NaN,
-// and clamps only then.
+// conversion costs four operations per element, so with up to 4 slots each
+// chunk is converted without it and stored at once, four results at a time
+// (no chunk's float32 results outlive its conversion), while the lane tracks
+// its largest magnitude; only if some lane of the wave saw a result beyond
+// 448 or a NaN does the wave convert its chunks again, saturated, and store
+// them over the first results (a lane's two stores to one address land in
+// program order).
 template <class IO, int V, bool ALIGNED>
 __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<IO> (&g)[V], const float (&r)[V],
                                             const bool (&isq)[V], const int (&col)[V], const int (&cnt)[V],
                                             char* yq_row, char* yk_row, bool active) {
   constexpr int VW = IO::kVW;
   if (IO::kDtype == kDtypeFP8 && V <= 4) {
-    float y[V][VW];
     float big = 0.0f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      float xf[VW], gf[VW];
-      decode<IO>(xv[i], xf);
-      decode_gamma<IO>(g[i], gf);
+      Chunk out;
 #pragma unroll
-      for (int e = 0; e < VW; ++e) y[i][e] = (xf[e] * gf[e]) * r[i];
-      if (cnt[i] > 0) big = __builtin_elementwise_maximum(big, max_abs(y[i]));  // idle slots left out
+      for (int p = 0; p < 4; ++p) {  // elements 4p .. 4p+3: one word of x, two of gamma
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], true);
+        const float y0 = (lo[0] * bf16_lo(g[i].w[2 * p])) * r[i];
+        const float y1 = (lo[1] * bf16_hi(g[i].w[2 * p])) * r[i];
+        const float y2 = (hi[0] * bf16_lo(g[i].w[2 * p + 1])) * r[i];
+        const float y3 = (hi[1] * bf16_hi(g[i].w[2 * p + 1])) * r[i];
+        float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(big, __builtin_fabsf(y0)),
+                                                __builtin_fabsf(y1));
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(y2)), __builtin_fabsf(y3));
+        big = cnt[i] > 0 ? m : big;  // idle slots left out
+        out.w[p] = pack_fp8_word(y0, y1, y2, y3);
+        // The word is formed here, not sunk into the store's branch (which
+        // would keep all of the chunk's float32 results live until then).
+        asm volatile("" : "+v"(out.w[p]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
     }
     // A NaN (from gamma, say) sends the wave through the saturating path too,
     // which keeps NaN and clamps the rest.
-    const bool clamp = __builtin_amdgcn_ballot_w64(active && !(big <= 448.0f)) != 0;
+    if (__builtin_amdgcn_ballot_w64(active && !(big <= 448.0f)) != 0) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      if (clamp) {
+      for (int i = 0; i < V; ++i) {
+        float xf[VW], gf[VW], y[VW];
+        decode<IO>(xv[i], xf);
+        decode_gamma<IO>(g[i], gf);
 #pragma unroll
-        for (int e = 0; e < VW; ++e) y[i][e] = sat_e4m3(y[i][e]);
+        for (int e = 0; e < VW; ++e) y[e] = sat_e4m3((xf[e] * gf[e]) * r[i]);
+        Chunk out;
+        pack<IO>(out, y);
+        if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
       }
-      Chunk out;
-      pack<IO>(out, y[i]);
-      if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
     }
   } else {
 #pragma unroll
@@ -466,15 +478,21 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   // were not faster). Each block still covers every gridDim-th group after its
   // first, so every group is covered once.
   // Large fused and apply launches: the blocks of the first resident
-  // generation start at 8 staggered times, 128 clocks apart (groups of 8
-  // consecutive blocks, one per XCD). Started together, that generation's
-  // reads are served interleaved and its blocks all finish at once, and the
-  // burst of scaling work then delays the next generation's loads. Staggered,
-  // apply launches ran 1.6% faster (bf16 and FP8 rows), fused FP8 rows about
-  // as much, fused bf16 rows unchanged.
-  if (MODE != MODE_STATS && a.stagger && blockIdx.x < 2048) {
-    const int k = (blockIdx.x >> 3) & 7;
-    for (int q = 0; q < k; ++q) __builtin_amdgcn_s_sleep(2);
+  // generation issue their gamma loads and then start their rows at 8
+  // staggered times, 128 clocks apart (groups of 8 consecutive blocks, one
+  // per XCD). Started together, that generation's reads are served
+  // interleaved and its blocks all finish at once, and the burst of scaling
+  // work then delays the next generation's loads. Staggered, apply launches
+  // ran 1.6% faster (bf16 and FP8 rows) and fused FP8 rows about as much;
+  // fused bf16 rows were unchanged. Only the 3-slot 16-byte kernels of bf16
+  // and FP8 rows carry it (where it was measured): in other kernels the
+  // extra code changed the register allocation, and several lost a wave per
+  // SIMD (fp32 rows in 6 slots, for one, ran up to 15% slower).
+  if constexpr (MODE != MODE_STATS && ALIGNED && V == 3 && IO::kBytes < 4) {
+    if (a.stagger && blockIdx.x < 2048) {
+      const int k = (blockIdx.x >> 3) & 7;
+      for (int q = 0; q < k; ++q) __builtin_amdgcn_s_sleep(2);
+    }
   }
   int64_t g0 = blockIdx.x;
   if (MODE == MODE_STATS && (int64_t)blockIdx.x < ((int64_t)gridDim.x & ~(int64_t)63)) {
