@@ -85,6 +85,7 @@ class CeilingLib:
 
 # (chunks per thread, threads per block) tried for the ceiling of each call
 CEIL_CONFIGS = ((1, 256), (2, 256), (3, 256), (4, 256), (1, 512), (2, 512), (1, 1024), (2, 1024))
+SHAPES_CEIL_CONFIGS = ((1, 256), (1, 512), (2, 512))  # the shapes that win in the full sweeps
 
 
 def _current_stream():
@@ -640,7 +641,9 @@ def shapes_table(dev, T=8192, steps=100):
     `us` is GPU time per call: `steps` calls over the rotating buffer sets
     replayed from a HIP graph, best of three replays (at the narrow widths a
     call from Python costs more host time than the kernel takes, so
-    back-to-back launches, `us_back_to_back`, do not keep the GPU busy)."""
+    back-to-back launches, `us_back_to_back`, do not keep the GPU busy).
+    `ceiling_us` is the streaming ceiling of the same bytes (the copy kernel
+    of libstreamceil.so over the same buffers, best of three launch shapes)."""
     import torch
     import layerwise_qk_norm_qknorm_amd as qk
     from layerwise_qk_norm_qknorm_amd import inputs as I
@@ -677,13 +680,17 @@ def shapes_table(dev, T=8192, steps=100):
                 best = t if best is None else min(best, t)
             plan = (qk.describe_headwise_plan(hq, hk, T, head_dim, dtype, 0, ld=w.ld) if head_dim
                     else qk.describe_plan(0, hq, hk, T, dtype, 1, ld=w.ld))
+            del graph
+            _, ceil = ceiling_sweep(step, dev, steps, 50, SHAPES_CEIL_CONFIGS, verbose=False)
             row = {"workload": w.key, "call": step.name, "head_dim": head_dim, "dtype": dtype, "tokens": T,
                    "hq": hq, "hk": hk, "hv": hv, "plan": plan, "us": best * 1e6,
                    "us_back_to_back": b2b * 1e6, "bytes": step.bytes, "GBps": step.bytes / best / 1e9,
-                   "frac_of_peak": step.bytes / best / 1e9 / HBM_PEAK_GBPS}
+                   "frac_of_peak": step.bytes / best / 1e9 / HBM_PEAK_GBPS,
+                   "ceiling_us": ceil["us"], "ceiling_launch": f"{ceil['per']}x{ceil['block']}",
+                   "frac_of_ceiling": ceil["us"] / (best * 1e6)}
             rows.append(row)
             print(json.dumps(row), flush=True)
-            del graph, step
+            del step
             torch.cuda.empty_cache()
     return rows
 

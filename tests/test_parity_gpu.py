@@ -466,8 +466,14 @@ def test_tensor_parallel_emulation_on_one_gpu(ranks):
     ref_p = oracle.qknorm_partial_stats(inp.q, inp.k, "bf16", ranks)
     got_p = planes.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got_p - ref_p) <= 1e-5 * ref_p)
-    fq_np, yq_np = torch_to_np(fq), torch_to_np(yq)
-    assert np.mean(fq_np == yq_np) > 0.99     # same math, same rounding almost everywhere
+    # fused(S = ranks) computes the same factors with its own float32
+    # summation order, so every output is the ranks' bf16 value or one of its
+    # two neighbours, and a differing factor rounds differently only next to a
+    # bf16 rounding boundary (a few elements in 10^4)
+    for name, fused, split, want in (("Q", fq, yq, ref.yq_bits), ("K", fk, yk, ref.yk_bits)):
+        check_bf16(torch_to_np(fused), want, f"fused(S = {ranks}) {name}")
+        exact, dmax = check_bf16(torch_to_np(fused), torch_to_np(split), f"fused(S = {ranks}) vs ranks {name}")
+        assert dmax <= 1 and exact >= 0.999, (name, exact, dmax)
     _log(f"[parity] tensor-parallel emulation, {ranks} ranks: slices match the full-row oracle")
 
 
