@@ -242,11 +242,14 @@ def test_decode_plans_stay_within_8_waves(dtype, hq, hk, T):
 
 # Headwise prefill launches for 128-wide heads over the same widths (threads
 # per token, chunks per lane): each the fastest token width timed on MI355X
-# or within 3.4% of it. The narrowest rows, where every width timed the same
-# (host-bound launches), are pinned as they are.
+# or within 3.4% of it. The narrowest bf16 and fp32 rows, where every width
+# timed the same (host-bound launches), are pinned as they are; the
+# narrowest FP8 rows (10 heads of 8 chunks) take the per-head layout, 6
+# tokens of 80 lanes to a block: 7.5 us against 11.2 us for the best
+# token-wide launch (256 threads per token).
 HEADWISE_PREFILL_PLANS = {
     "bf16": [(64, 3), (192, 2), (256, 2), (384, 2), (512, 2), (576, 2), (768, 2), (1024, 2), (1024, 3), (832, 2)],
-    "fp8": [(256, 1), (192, 1), (128, 2), (192, 2), (192, 2), (256, 2), (192, 3), (256, 4), (192, 6), (256, 3)],
+    "fp8": [(80, 1), (192, 1), (128, 2), (192, 2), (192, 2), (256, 2), (192, 3), (256, 4), (192, 6), (256, 3)],
     "f32": [(192, 2), (384, 2), (640, 2), (832, 2), (1024, 2), (1024, 2), (1024, 3), (1024, 4), (1024, 6), (1024, 3)],
 }
 
@@ -257,6 +260,7 @@ def test_headwise_prefill_plans_are_the_measured_best(dtype):
     for (hq, hk, hv), (threads, slots) in zip(I.PREFILL_WIDTHS, HEADWISE_PREFILL_PLANS[dtype]):
         f = fields(qk.describe_headwise_plan(hq, hk, 8192, 128, dtype, 0, ld=hq + hk + hv))
         assert (int(f["threads/token"]), int(f["slots"])) == (threads, slots), (dtype, hq, hk, f)
+        assert f["layout"] == ("per-head" if (dtype, hq) == ("fp8", 1024) else "token-wide"), (dtype, hq, hk, f)
 
 
 # Per-head headwise prefill launches (heads whose chunk count is not a power
