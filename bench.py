@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,12 +65,13 @@ class CeilingLib:
     kernels (16-byte loads, non-temporal 16-byte stores) that give the
     practical HBM ceiling for the bytes a QK-Norm call moves."""
 
-    def __init__(self):
+    def __init__(self, path=None):
         import ctypes
         from layerwise_qk_norm_qknorm_amd import build_lib
-        if not os.path.exists(build_lib.CEIL_LIB):
-            raise RuntimeError(f"{build_lib.CEIL_LIB} is not built; run __graft_entry__.build()")
-        lib = ctypes.CDLL(build_lib.CEIL_LIB)
+        path = path or build_lib.CEIL_LIB
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.qkceil_stream.argtypes = [vp, i64, vp, i64, i64, i64, ci, ci, vp, vp]
         lib.qkceil_stream.restype = ci
@@ -695,6 +697,93 @@ def shapes_table(dev, T=8192, steps=100):
     return rows
 
 
+TIMELINE_CALLS = (("gqa_prefill", "fused"), ("gqa_prefill_fp8", "fused"), ("rank_slice", "partial"),
+                  ("rank_slice", "apply"), ("rank_slice_fp8", "partial"), ("rank_slice_fp8", "apply"))
+
+
+def timeline_summary(rec):
+    """Launch-shape figures from one launch's block records [grid, 3] (start
+    and end on the 100 MHz real-time counter, XCC id << 32 | hardware id):
+    all in microseconds from the first block's start."""
+    import numpy as np
+    if not (rec[:, 1] > 0).all():
+        raise RuntimeError(f"{int((rec[:, 1] == 0).sum())} of {len(rec)} blocks left no record")
+    start = rec[:, 0].astype(np.int64)
+    end = rec[:, 1].astype(np.int64)
+    t0 = start.min()
+    s, e = (start - t0) / 100.0, (end - t0) / 100.0
+    first_end = e.min()
+    first_gen = s < first_end          # blocks already running when the first one ends
+    xcc = (rec[:, 2] >> 32).astype(np.int64)
+    xcd_end = np.array([e[xcc == x].max() for x in np.unique(xcc)])
+    return {"blocks": int(len(s)), "span_us": float(e.max()), "first_generation_blocks": int(first_gen.sum()),
+            "first_generation_start_spread_us": float(s[first_gen].max()), "first_block_end_us": float(first_end),
+            "median_block_us": float(np.median(e - s)), "last_block_start_us": float(s.max()),
+            "last_start_to_end_us": float(e.max() - s.max()), "xcds": int(len(xcd_end)),
+            "last_xcd_after_median_xcd_us": float(xcd_end.max() - np.median(xcd_end))}
+
+
+def timeline(dev, reps=5):
+    """Per-block start and end clocks of single launches inside a stream of
+    launches, from the timing-only builds (libqknorm_clocks.so in place of
+    libqknorm.so, libstreamceil_clocks.so for the ceiling at 1 chunk x 512
+    threads): one JSON line per call and kernel, the median of `reps`
+    launches of each figure of timeline_summary."""
+    import ctypes
+    import numpy as np
+    import torch
+    from layerwise_qk_norm_qknorm_amd import binding, build_lib
+    from layerwise_qk_norm_qknorm_amd import inputs as I
+    if binding._lib is not None:
+        raise RuntimeError("--timeline must load libqknorm_clocks.so before any other library call")
+    if os.environ.get("QKNORM_MAX_GRID"):
+        raise RuntimeError("--timeline takes one block per token group (QKNORM_MAX_GRID must be unset)")
+    for path in (build_lib.CLOCKS_LIB, build_lib.CEIL_CLOCKS_LIB):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+    binding._LIB_PATH = build_lib.CLOCKS_LIB
+    qk = binding.load_library()
+    qk.qknorm_set_block_clocks.argtypes = [ctypes.c_void_p]
+    ceil = CeilingLib(build_lib.CEIL_CLOCKS_LIB)
+    ceil.lib.qkceil_set_block_clocks.argtypes = [ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rows = []
+    for wl, call in TIMELINE_CALLS:
+        w = I.WORKLOADS[wl]
+        inp = I.make_inputs(w)
+        step = {"fused": FusedStep, "partial": PartialStep, "apply": ApplyStep}[call]
+        step = step(w, inp, dev, 1) if call == "fused" else step(w, inp, dev)
+        plan = _plan_text(binding, w, step.name, 1)
+        tpb = int(re.search(r"tokens/block=(\d+)", plan).group(1))
+        cs = CeilingStep(step, ceil, 1, 512, sink.data_ptr())
+        if cs.launches != 1:
+            raise RuntimeError(f"{wl}: the ceiling takes {cs.launches} launches; one is timed")
+        chunks = step.stream_bytes // (2 if step.copy else 1) // 16
+        for kind, st, grid, setter in (("kernel", step, -(-w.T // tpb), qk.qknorm_set_block_clocks),
+                                       ("ceiling", cs, -(-chunks // 512), ceil.lib.qkceil_set_block_clocks)):
+            _, ev = time_steps(st, 200, 300, graph=False)   # warm-up, and the eager rate of this build
+            runs = []
+            for rep in range(reps):
+                buf = torch.zeros(grid * 3, dtype=torch.int64, device=dev)
+                for i in range(30):
+                    st(i)
+                setter(buf.data_ptr())
+                st(30)
+                setter(None)
+                for i in range(31, 40):
+                    st(i)
+                torch.cuda.synchronize()
+                runs.append(timeline_summary(buf.cpu().numpy().reshape(grid, 3)))
+            med = {k: float(np.median([r[k] for r in runs])) for k in runs[0]}
+            row = {"workload": wl, "call": step.name, "kernel": kind, "grid": grid,
+                   "plan": plan if kind == "kernel" else cs.name, "eager_us_per_launch": ev / 200 * 1e6, **med}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+        del step, cs
+        torch.cuda.empty_cache()
+    return rows
+
+
 def _plan_text(qk, w, call, shards):
     if call == "qknorm_headwise":
         return qk.describe_headwise_plan(w.hq, w.hk, w.T, w.head_dim, w.dtype, 0, ld=w.ld)
@@ -723,6 +812,9 @@ def main():
     ap.add_argument("--record-traffic", nargs="+", metavar="PMC_DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc output directories "
                          "(no GPU needed)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-block start/end clocks of single launches of the headline calls and their ceilings, "
+                         "from the timing-only builds (one JSON line per call and kernel)")
     ap.add_argument("--latency", action="store_true",
                     help="per-call times of the tiny, small-dense and decode workloads (one JSON line each)")
     ap.add_argument("--shapes", action="store_true",
@@ -749,6 +841,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+    if args.timeline:   # loads the timing-only library in place of libqknorm.so
+        log(f"[bench] device {torch.cuda.get_device_name(0)}; block clocks from the timing-only builds")
+        timeline(dev)
+        return
     qk.load_library()
     log(f"[bench] device {torch.cuda.get_device_name(0)}; library {qk.library_path()}")
 

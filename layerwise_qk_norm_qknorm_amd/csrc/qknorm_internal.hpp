@@ -98,6 +98,9 @@ struct RowArgs {
   const float* stats; // MODE_APPLY: [P][2][T]
   int n_planes;
   int stagger;        // 1: the first resident generation of blocks starts staggered (large launches)
+#ifdef QKNORM_BLOCK_CLOCKS
+  unsigned long long* clocks;  // timing-only builds: per block {start, end, XCC id << 32 | hardware id}
+#endif
 };
 
 // Headwise kernel arguments: every head of head_dim columns is normalized on

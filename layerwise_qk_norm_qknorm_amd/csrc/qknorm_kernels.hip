@@ -40,6 +40,28 @@
 namespace qkn {
 namespace {
 
+#ifdef QKNORM_BLOCK_CLOCKS
+// Timing-only builds (libqknorm_clocks.so, which bench.py --timeline loads in
+// place of libqknorm.so): thread 0 of every block records the 100 MHz
+// real-time counter when the block starts and, once all of the block's loads
+// and stores have completed, when it ends, with the XCC and hardware ids of
+// the CU it ran on (the block's record: 3 words).
+__device__ __forceinline__ void clock_begin(unsigned long long* c) {
+  if (c && threadIdx.x == 0) c[3 * (size_t)blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void clock_end(unsigned long long* c) {
+  if (!c) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    c[3 * (size_t)blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+    const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    c[3 * (size_t)blockIdx.x + 2] = ((unsigned long long)xcc << 32) | hw;
+  }
+}
+#endif
+
 // I/O types. kVW: elements per 16-byte row chunk; kBytes: bytes per row
 // element; kGW / kGBytes: 32-bit words of gamma per chunk and bytes per gamma
 // element (FP8 rows take bf16 gamma).
@@ -424,6 +446,9 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 template <class IO, int V, int MODE, bool ALIGNED, bool WW>
 __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_rows(const RowArgs a) {
   extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token] float2 (Q, K)
+#ifdef QKNORM_BLOCK_CLOCKS
+  clock_begin(a.clocks);
+#endif
   constexpr int VW = IO::kVW;
   const int tid = threadIdx.x;
   const int G = a.tok_threads;
@@ -609,6 +634,9 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       scale_store<IO, V, ALIGNED>(xv, g, rr, isq, col, cnt, yq_row, yk_row, active);
     }
   }
+#ifdef QKNORM_BLOCK_CLOCKS
+  clock_end(a.clocks);
+#endif
 }
 
 // Headwise QK-Norm (the introduction's per-head granularity): Eq. 1 for every
@@ -884,6 +912,10 @@ KernelFn pick_kernel(const Plan& p) {
 
 }  // namespace
 
+#ifdef QKNORM_BLOCK_CLOCKS
+static unsigned long long* g_block_clocks = nullptr;  // the next row launches' block records (or none)
+#endif
+
 int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   KernelFn fn = pick_kernel(p);
   if (!fn) {
@@ -899,6 +931,9 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   // an earlier, unrelated call is reported as ours).
   RowArgs a = args;
   a.stagger = grid >= 4096 ? 1 : 0;  // only launches of at least two resident generations
+#ifdef QKNORM_BLOCK_CLOCKS
+  a.clocks = g_block_clocks;
+#endif
   void* kargs[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
                                        dim3((unsigned)p.threads), kargs, (size_t)p.lds_bytes,
@@ -935,3 +970,12 @@ int launch_heads(const Plan& p, const HeadArgs& args, void* stream, std::string*
 }
 
 }  // namespace qkn
+
+#ifdef QKNORM_BLOCK_CLOCKS
+// Timing-only builds: the device buffer (3 words per block of the grid) that
+// the following row launches (fused, partial_stats, apply_with_stats) write
+// their block records into, or NULL for none.
+extern "C" void qknorm_set_block_clocks(void* clocks) {
+  qkn::g_block_clocks = static_cast<unsigned long long*>(clocks);
+}
+#endif

@@ -22,6 +22,12 @@
 //     Returns 0, or 1 for an invalid argument (nothing launched) and 3 for a
 //     launch failure; the message is in qkceil_last_error().
 //   const char* qkceil_last_error(void);
+//
+// Built with QKNORM_BLOCK_CLOCKS (libstreamceil_clocks.so, for bench.py
+// --timeline), the kernel also records per block the 100 MHz real-time
+// counter at its start and, once its loads and stores have completed, at its
+// end, with the XCC and hardware ids of its CU, into the buffer set by
+//   void qkceil_set_block_clocks(void* clocks);   (3 words per block, or NULL)
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,11 +39,21 @@ namespace {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 thread_local std::string g_err;
+#ifdef QKNORM_BLOCK_CLOCKS
+unsigned long long* g_clocks = nullptr;
+#endif
 
 template <int PER, bool COPY>
 __global__ void __launch_bounds__(1024) stream_rows(const char* __restrict__ x, int64_t ldx, char* __restrict__ y,
                                                      int64_t ldy, uint32_t nc, uint32_t total,
-                                                     uint32_t* __restrict__ sink) {
+                                                     uint32_t* __restrict__ sink
+#ifdef QKNORM_BLOCK_CLOCKS
+                                                     , unsigned long long* clocks
+#endif
+) {
+#ifdef QKNORM_BLOCK_CLOCKS
+  if (clocks && threadIdx.x == 0) clocks[3 * (size_t)blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+#endif
   const uint32_t b = blockDim.x;
   const uint32_t first = blockIdx.x * PER * b + threadIdx.x;
   u32x4_t v[PER];
@@ -65,6 +81,18 @@ __global__ void __launch_bounds__(1024) stream_rows(const char* __restrict__ x, 
     for (int k = 0; k < PER; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     if (acc == 0x9E3779B9u) *sink = acc;  // data-dependent, so the loads stay
   }
+#ifdef QKNORM_BLOCK_CLOCKS
+  if (clocks) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      clocks[3 * (size_t)blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+      const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+      const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+      clocks[3 * (size_t)blockIdx.x + 2] = ((unsigned long long)xcc << 32) | hw;
+    }
+  }
+#endif
 }
 
 template <bool COPY>
@@ -91,6 +119,10 @@ extern "C" {
 
 const char* qkceil_last_error(void) { return g_err.c_str(); }
 
+#ifdef QKNORM_BLOCK_CLOCKS
+void qkceil_set_block_clocks(void* clocks) { g_clocks = static_cast<unsigned long long*>(clocks); }
+#endif
+
 int qkceil_stream(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t row_bytes, int per,
                   int block, void* sink, void* stream) {
   if (!x || (!y && !sink)) return bad("x, and y or sink, are required");
@@ -109,7 +141,12 @@ int qkceil_stream(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows
   char* yp = static_cast<char*>(y);
   uint32_t nc32 = (uint32_t)nc, total32 = (uint32_t)total;
   uint32_t* sp = static_cast<uint32_t*>(sink);
+#ifdef QKNORM_BLOCK_CLOCKS
+  unsigned long long* cp = g_clocks;
+  void* args[] = {&xp, &ldx, &yp, &ldy, &nc32, &total32, &sp, &cp};
+#else
   void* args[] = {&xp, &ldx, &yp, &ldy, &nc32, &total32, &sp};
+#endif
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, 0,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

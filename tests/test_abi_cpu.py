@@ -43,6 +43,25 @@ def test_every_declared_symbol_is_exported():
         assert re.search(rf"\bT {name}$", out, re.M), name
 
 
+def test_block_clocks_only_in_the_timing_build():
+    """The block-clock hook exists only in the timing-only twin that
+    bench.py --timeline loads; the library the boundary ships has none, and
+    both export the same calls otherwise."""
+    from layerwise_qk_norm_qknorm_amd import build_lib
+    if not os.path.exists(build_lib.CLOCKS_LIB):
+        pytest.skip("libqknorm_clocks.so not built")
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+        return {l.split()[-1] for l in out.splitlines() if " T " in l}
+
+    product, timing = exported(qk.library_path()), exported(build_lib.CLOCKS_LIB)
+    assert "qknorm_set_block_clocks" not in product
+    assert timing - product == {"qknorm_set_block_clocks"}
+    for name in declared_functions():
+        assert name in timing, name
+
+
 def test_abi_version():
     assert qk.abi_version() == 3
 
