@@ -456,13 +456,18 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
     if (few_tokens) {
       score = (v > 2 ? (v - 2) : (2 - v)) + (wfrac > 0.25 ? 8.0 : 0.0) + 2.0 * wfrac + (waves > 8 ? 1.5 : 0.0) -
               0.01 * waves;
-    } else if (dtype == kDtypeBF16 && mode == MODE_FUSED && T <= 4096) {
+    } else if (dtype == kDtypeBF16 && mode != MODE_APPLY && T <= 4096) {
       // Mid-size fused bf16 launches (1024 to 4096 tokens, the range timed)
       // run best over fewer waves with 3 to 6 chunks per lane, whether their
       // rows stream from HBM or sit in the last-level cache (timed with and
       // without rotating buffers at T = 512 to 4096: 1.8% from the fastest
       // layout on average, against 3.6% and 11% for the rule below). Larger
-      // launches and the split calls keep the prefill rule.
+      // launches and apply_with_stats keep the prefill rule. partial_stats
+      // takes the fused call's layout: the lanes per shard and chunks per
+      // lane fix the order in which a shard's squares are added, and the
+      // split path must add them as the fused call does to reproduce it bit
+      // for bit (apply_with_stats adds nothing within a row, so its layout
+      // is free).
       score = (v == 3 || v == 4 ? 0.0 : v == 6 ? 0.1 : v == 2 ? 0.3 : v == 8 ? 0.4 : v == 1 ? 10.0 : 1.0) +
               (wfrac > 0.25 ? 8.0 : 2.0 * wfrac) + (waves > 4 ? 0.3 : 0.0) + (waves >= 13 ? 3.0 : 0.0) +
               0.01 * waves;

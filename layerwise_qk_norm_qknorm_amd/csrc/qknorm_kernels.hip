@@ -244,9 +244,9 @@ __device__ __forceinline__ void store_chunk(char* row, int col, int n, const Chu
 // use the gfx950 two-way bf16 dot product with a float32 accumulator, two
 // squares per instruction straight from the packed words (products exact,
 // denormal products kept), and FP8 rows first widen each pair of E4M3 values
-// exactly to a bf16 pair for the same dot product. Without DOT (where the
-// kernel widens the chunk to float32 for the scaling anyway and keeps it) and
-// for fp32 rows: a chain of fused multiply-adds in element order.
+// exactly to a bf16 pair for the same dot product. Without DOT (headwise
+// kernels that widen the chunk to float32 for the scaling anyway and keep it)
+// and for fp32 rows: a chain of fused multiply-adds in element order.
 template <class IO, bool DOT>
 __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
   float s = 0.0f;
@@ -273,14 +273,26 @@ __device__ __forceinline__ float chunk_sumsq(const Chunk& c) {
   return s;
 }
 
-// Whether a kernel with V chunk slots that also scales (SCALES) takes the dot
-// product sums: packed rows held in up to 2 (bf16) or 4 (FP8) slots stay
-// widened to float32 from the sums to the scaling, so their sums reuse that
-// widening (measured faster there); above that, and for partial_stats, the
-// rows are widened again for the scaling and the dot products save the work.
-template <class IO, int V, bool SCALES>
-constexpr bool sums_by_dot() {
-  return IO::kBytes < 4 && !(SCALES && V <= (IO::kBytes == 2 ? 2 : 4));
+// The layerwise row kernels sum bf16 and FP8 rows by dot products in every
+// mode and for every slot count. The fused call and partial_stats must add
+// the same values in the same order, or the split path (partial_stats, then
+// apply_with_stats) would not reproduce the fused call bit for bit: a chain
+// of fused multiply-adds rounds after every square, the dot product after
+// every pair, and the two differ in the last bit of about 1% of bf16 chunk
+// sums (and of FP8 chunks that mix large and small magnitudes).
+template <class IO>
+constexpr bool row_sums_by_dot() {
+  return IO::kBytes < 4;
+}
+
+// The headwise kernels have no split path to agree with: packed rows held in
+// up to 2 (bf16) or 4 (FP8) slots stay widened to float32 from the sums to the
+// scaling, so their sums reuse that widening (measured faster there); above
+// that the rows are widened again for the scaling and the dot products save
+// the work.
+template <class IO, int V>
+constexpr bool head_sums_by_dot() {
+  return IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4);
 }
 
 // Phase B and the final scaling for this lane's chunks of one token:
@@ -547,7 +559,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       float aq = 0.0f, ak = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const float cs = cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, MODE != MODE_STATS>()>(xv[i]) : 0.0f;
+        const float cs = cnt[i] > 0 ? chunk_sumsq<IO, row_sums_by_dot<IO>()>(xv[i]) : 0.0f;
         aq += isq[i] ? cs : 0.0f;
         ak += isq[i] ? 0.0f : cs;
       }
@@ -617,10 +629,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
 
     if constexpr (MODE != MODE_STATS) {
-      // Packed rows widened once for the sums are widened again for the
-      // scaling above a few slots (bf16: 2, FP8: 4), so that only the packed
-      // words stay live across the exchange: fewer registers, more waves.
-      if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {
+      // Packed rows are widened for the scaling only after the exchange, so
+      // that only the packed words stay live across it: fewer registers,
+      // more waves.
+      if (IO::kBytes < 4) {
 #pragma unroll
         for (int i = 0; i < V; ++i) keep_packed(xv[i]);
       }
@@ -703,7 +715,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, true>()>(xv[i]) : 0.0f;
+    for (int i = 0; i < V; ++i) acc += cnt[i] > 0 ? chunk_sumsq<IO, head_sums_by_dot<IO, V>()>(xv[i]) : 0.0f;
     acc = group_sum(acc, L);
 
     {
@@ -785,7 +797,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     float ss[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
-      ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO, sums_by_dot<IO, V, true>()>(xv[i]) : 0.0f, nc);
+      ss[i] = group_sum(cnt[i] > 0 ? chunk_sumsq<IO, head_sums_by_dot<IO, V>()>(xv[i]) : 0.0f, nc);
 
     {
       if (IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4)) {

@@ -127,6 +127,28 @@ def test_fused_equals_split_fp8_bitwise():
     assert torch.equal(fk.view(torch.uint8), ak.view(torch.uint8))
 
 
+@pytest.mark.parametrize("key,T,shards", [("gqa_prefill_fp8", 1024, 1), ("gqa_prefill_fp8", 2048, 2),
+                                          ("rank_slice_fp8", 4096, 1)])
+def test_fused_equals_split_fp8_bitwise_with_outliers(key, T, shards):
+    """Rows of 3 or 4 chunks per lane, where the fused kernel once summed FP8
+    squares by fused multiply-adds and partial_stats by dot products: the
+    outlier draws (x50) put large and small squares in one chunk, where the
+    two roundings differ."""
+    w = I.WORKLOADS[key].with_T(T)
+    inp = I.make_inputs(w)
+    _log(f"[case] fused == split {key} T={T} S={shards}")
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    fq, fk = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_fused(xq, xk, gq, gk, w.eps, shards, fq, fk)
+    part = qk.qknorm_partial_stats(xq, xk, shards)
+    aq, ak = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, w.eps, part, inp.q.shape[1], inp.k.shape[1], aq, ak)
+    torch.cuda.synchronize()
+    assert torch.equal(fq.view(torch.uint8), aq.view(torch.uint8))
+    assert torch.equal(fk.view(torch.uint8), ak.view(torch.uint8))
+
+
 def test_headwise_fp8():
     w = I.GQA_PREFILL_FP8.with_T(1024)
     inp = I.make_inputs(w)

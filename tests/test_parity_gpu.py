@@ -189,6 +189,21 @@ def test_fused_equals_partial_stats_plus_apply_bitwise(key, shards):
     _check_fused_equals_split(I.make_inputs(I.WORKLOADS[key]), shards)
 
 
+# Layouts where fused and split once disagreed: 2 chunks per lane (decode
+# rows, S = 1), where the fused kernel summed squares by fused multiply-adds
+# and partial_stats by dot products, and mid-size bf16 launches (1024 to 4096
+# tokens), where partial_stats took another lane layout than the fused call.
+# The GQA prefill draws (0.1% of elements x50) mix large and small squares in
+# one chunk, which is where the two ways of adding them differ.
+@pytest.mark.parametrize("key,T,shards", [("decode_t256", 256, 1), ("gqa_prefill", 2048, 1),
+                                          ("gqa_prefill", 1536, 2), ("gqa_prefill", 4096, 1)])
+def test_fused_equals_split_where_layouts_once_differed(key, T, shards):
+    w = I.WORKLOADS[key].with_T(T)
+    _log(f"[case] fused == split {key} T={T} S={shards} "
+         f"plan: {qk.describe_plan(0, w.hq, w.hk, w.T, w.dtype, shards, ld=w.ld)}")
+    _check_fused_equals_split(I.make_inputs(w), shards)
+
+
 @pytest.mark.parametrize("dtype,shards", [("bf16", 64), ("bf16", 32), ("bf16", 16), ("f32", 64)])
 def test_many_shards_fused_equals_partial_stats_plus_apply_bitwise(dtype, shards):
     """Narrow shards (4 to 16 lanes each) put 16 to 64 lane groups of one

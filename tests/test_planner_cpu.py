@@ -160,17 +160,44 @@ def test_prefill_plans_are_the_measured_best(dtype):
 
 # A mid-size fused bf16 launch (T = 1536, rows 4096/4096): the mid-size rule's
 # 256 lanes x 4 chunks; the prefill rule's 384 x 3 timed 12 to 32% slower on
-# MI355X for these rows (the worst case of that rule at mid sizes). The split calls and launches above 4096
-# tokens keep the prefill rule (only fused launches of 1024 to 4096 tokens
-# were timed for the mid-size rule).
+# MI355X for these rows (the worst case of that rule at mid sizes). partial_stats
+# takes the same layout (its sums must be added as the fused call adds them);
+# apply_with_stats and launches above 4096 tokens keep the prefill rule (only
+# fused launches of 1024 to 4096 tokens were timed for the mid-size rule).
 def test_mid_size_fused_bf16_plan():
-    f = fields(qk.describe_plan(0, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
-    assert (int(f["lanes/shard"]), int(f["slots"])) == (256, 4), f
-    for op in (1, 2):
-        g = fields(qk.describe_plan(op, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
-        assert (int(g["lanes/shard"]), int(g["slots"])) == (384, 3), (op, g)
+    for op in (0, 1):
+        f = fields(qk.describe_plan(op, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
+        assert (int(f["lanes/shard"]), int(f["slots"])) == (256, 4), (op, f)
+    g = fields(qk.describe_plan(2, 4096, 4096, 1536, "bf16", 1, ld=3 * 4096))
+    assert (int(g["lanes/shard"]), int(g["slots"])) == (384, 3), g
     h = fields(qk.describe_plan(0, 4096, 4096, 6144, "bf16", 1, ld=3 * 4096))
     assert (int(h["lanes/shard"]), int(h["slots"])) == (384, 3), h
+
+
+# The split path reproduces the fused call bit for bit only if partial_stats
+# adds each shard's squares in the fused call's order: the same path, lanes per
+# shard and chunks per lane (which fix the in-lane order and the lane
+# butterfly) for every shape, shard count, token count and alignment.
+@settings(max_examples=400, deadline=None, derandomize=True)
+@given(dtype=st.sampled_from(["bf16", "f32", "fp8"]), shards=st.sampled_from([1, 1, 2, 4, 8, 64]),
+       hq_s=st.integers(1, 6000), hk_s=st.integers(1, 2000),
+       T=st.sampled_from([1, 8, 256, 1023, 1024, 1536, 2048, 4096, 4097, 8192, 16384]), unaligned=st.booleans())
+def test_partial_stats_takes_the_fused_reduction_layout(dtype, shards, hq_s, hk_s, T, unaligned):
+    vw = VW[dtype]
+    if not unaligned:
+        hq_s, hk_s = ceil_div(hq_s, vw) * vw, ceil_div(hk_s, vw) * vw
+    hq, hk = hq_s * shards, hk_s * shards
+    ld = hq + hk + (1 if unaligned else 0)
+    try:
+        fused = fields(qk.describe_plan(0, hq, hk, T, dtype, shards, ld=ld))
+    except qk.QKNormError as e:
+        assert e.status == UNSUPPORTED
+        with pytest.raises(qk.QKNormError):
+            qk.describe_plan(1, hq, hk, T, dtype, shards, ld=ld)
+        return
+    stats = fields(qk.describe_plan(1, hq, hk, T, dtype, shards, ld=ld))
+    for key in ("path", "shards", "chunks", "lanes/shard", "slots"):
+        assert fused[key] == stats[key], (key, fused, stats)
 
 
 def prefill_candidates(nc, dtype):
