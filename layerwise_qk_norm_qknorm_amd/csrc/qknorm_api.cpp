@@ -206,8 +206,11 @@ int check_and_plan(int mode, const qknorm_operand_t* q, const qknorm_operand_t* 
       aligned = aligned && ((uintptr_t)o->y % 16 == 0) && (o->ld_y % vw == 0) && ((uintptr_t)o->gamma % 16 == 0);
   }
 
+  // Packed rows: K starts right after Q's last column, with the same stride.
+  const bool packed = (const char*)k->x == (const char*)q->x + q->h * esz && k->ld_x == q->ld_x;
+
   std::string why;
-  if (!qkn::make_plan(mode, dtype, aligned, shards, q->h, k->h, T, &out->plan, &why))
+  if (!qkn::make_plan(mode, dtype, aligned, packed, shards, q->h, k->h, T, &out->plan, &why))
     return fail(QKNORM_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
 
   qkn::RowArgs& a = out->args;
@@ -394,7 +397,7 @@ static double prefill_slot_cost(int dtype, int v) {
   }
 }
 
-bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* p, std::string* why) {
   Plan r;
   r.mode = mode;
@@ -505,6 +508,22 @@ bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_
     return false;
   }
   r.lds_bytes = r.waves > 1 ? 2 * r.tokens_per_block * groups_per_token * 2 * (int)sizeof(float) : 0;
+  // partial_stats of one shard of packed rows with 32- or 64-lane tokens and
+  // 2 to 4 chunks per lane on the 16-byte path (the rank slices) takes the
+  // slot-wave form: the same lanes, slots and sums, with each chunk loaded by
+  // a thread of its own in row order and the sums exchanged in LDS; a block
+  // holds one wave's worth of tokens, and each XCD takes runs of 32
+  // consecutive tokens (whole 128-byte lines of the partial planes). It has
+  // no token loop, so it takes launches of at most 2^30 tokens (one block per
+  // token group).
+  if (mode == MODE_STATS && aligned && packed && shards == 1 && (r.lanes == 32 || r.lanes == 64) &&
+      r.slots >= 2 && r.slots <= 4 && T <= ((int64_t)1 << 30)) {
+    r.slot_waves = 1;
+    r.tokens_per_block = 64 / r.lanes;
+    r.threads = 64 * r.slots;
+    r.lds_bytes = 0;  // static: 2 x slots x 64 floats
+    r.xrun = 32 / r.tokens_per_block;
+  }
   *p = r;
   return true;
 }
@@ -660,13 +679,15 @@ std::string describe(const Plan& p) {
              p.tokens_per_block, p.threads, p.slots);
     return buf;
   }
-  char buf[320];
-  snprintf(buf, sizeof buf,
-           "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads/token=%d "
-           "tokens/block=%d waves/token=%d slots=%d lds=%d",
-           p.mode == MODE_FUSED ? "fused" : p.mode == MODE_STATS ? "partial_stats" : "apply_with_stats",
-           dtype_name(p.dtype), p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
-           p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
+  char buf[384];
+  int n = snprintf(buf, sizeof buf,
+                   "%s %s path=%s shards=%d shard_w=(%d,%d) chunks=(%d,%d) lanes/shard=%d threads/token=%d "
+                   "tokens/block=%d waves/token=%d slots=%d lds=%d",
+                   p.mode == MODE_FUSED ? "fused" : p.mode == MODE_STATS ? "partial_stats" : "apply_with_stats",
+                   dtype_name(p.dtype), p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
+                   p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
+  if (p.slot_waves && n > 0 && n < (int)sizeof buf)
+    snprintf(buf + n, sizeof buf - n, " form=slot-waves threads/block=%d xcd_run=%d", p.threads, p.xrun);
   return buf;
 }
 

@@ -71,6 +71,12 @@ struct Plan {
   int heads_k = 0;
   int head_dim = 0;
   int heads_packed = 0;  // 1: token-wide chunk layout, one nc-lane group per head per slot
+  // partial_stats only: 1 for the slot-wave form (a chunk per thread, the
+  // chunk sums exchanged in LDS; see qknorm_stats_slot_waves), with runs of
+  // 8 * xrun blocks ordered so that each XCD takes xrun consecutive blocks of
+  // tokens
+  int slot_waves = 0;
+  int xrun = 0;
 };
 
 // Kernel arguments (passed by value).
@@ -137,7 +143,9 @@ int launch_heads(const Plan& plan, const HeadArgs& args, void* stream, std::stri
 
 // Fills `plan` for the given shapes; returns false (with a reason) if no
 // compiled kernel can hold the row.
-bool make_plan(int mode, int dtype, bool aligned, int shards, int64_t hq, int64_t hk, int64_t T,
+// packed: Q and K are adjacent column ranges of the same rows (K's first
+// element right after Q's last, one row stride).
+bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64_t hq, int64_t hk, int64_t T,
                Plan* plan, std::string* why);
 
 std::string describe(const Plan& p);

@@ -14,6 +14,7 @@ ROW_CASES = [
     (1500, 640, 128, "bf16", 1),       # 32 lanes per token, 8 tokens per block
     (999, 2048, 512, "fp8", 4),        # FP8, four shards in one wave (few tokens: one slot)
     (777, 1024, 256, "f32", 2),        # fp32, two shards over two waves
+    (1501, 1280, 256, "fp8", 1),       # FP8 32-lane tokens; partial_stats in the slot-wave form
 ]
 HEAD_CASES = [128, 72]                 # token-wide and per-head kernels
 

@@ -89,6 +89,13 @@ def test_layerwise_plans_fit_their_kernels(dtype, shards, hq_s, hk_s, T, op, una
     if G % 64:                                       # several tokens per wave
         assert G < 64 and 64 % G == 0 and shards == 1 and T >= 1024
     assert tpb >= 1 and (tpb == 1 or G <= 64)
+    if f.get("form") == "slot-waves":
+        # partial_stats, one shard, a token of 32 or 64 lanes: one wave per
+        # chunk slot of a wave's lanes, one wave's worth of tokens per block
+        assert op == 1 and shards == 1 and aligned and lanes in (32, 64) and 2 <= slots <= 4
+        assert tpb == 64 // lanes and int(f["threads/block"]) == 64 * slots and lds == 0
+        assert int(f["xcd_run"]) * tpb == 32
+        return
     assert tpb * G <= max_threads(slots, dtype, aligned)
     waves = ceil_div(G, 64)
     group = min(lanes, 64)
