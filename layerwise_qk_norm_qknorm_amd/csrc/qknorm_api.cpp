@@ -521,7 +521,7 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
     r.slot_waves = 1;
     r.tokens_per_block = 64 / r.lanes;
     r.threads = 64 * r.slots;
-    r.lds_bytes = 0;  // static: 2 x slots x 64 floats
+    r.lds_bytes = 0;  // static: slots x 64 floats
     r.xrun = 32 / r.tokens_per_block;
   }
   *p = r;
