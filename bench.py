@@ -451,6 +451,8 @@ def _call_of(kernel_name):
             else "stream_read"
     if "qknorm_heads" in n:
         return "qknorm_headwise"
+    if "qknorm_stats_slot_waves<" in n:
+        return "qknorm_partial_stats"
     if "qknorm_rows<" in n:
         mode = n.split("qknorm_rows<")[1].split(">")[0].split(",")[2].strip()
         return {"0": "qknorm_fused", "1": "qknorm_partial_stats", "2": "qknorm_apply_with_stats"}.get(mode)
@@ -544,8 +546,10 @@ def record_traffic(workload, dirs, commands):
 def latency_table(dev, reps=200):
     """Per-call times of the small, launch- and latency-bound workloads:
     median of single calls bracketed by HIP events, the mean over
-    back-to-back calls from Python, and the mean over 100 calls replayed from
-    a HIP graph (GPU time per call; buffers stay cache resident at these sizes)."""
+    back-to-back calls from Python through the plain binding and through a
+    PreparedCall (arguments checked and marshalled once), the host time per
+    call of each, and the mean over 100 calls replayed from a HIP graph (GPU
+    time per call; buffers stay cache resident at these sizes)."""
     import torch
     import layerwise_qk_norm_qknorm_amd as qk
     from layerwise_qk_norm_qknorm_amd import inputs as I
@@ -579,6 +583,26 @@ def latency_table(dev, reps=200):
         for _ in range(20):
             call()
         torch.cuda.synchronize()
+        # host time per call: the binding's checks and marshalling, the
+        # library's validation and planning, and the launch
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            call()
+        host_us = (time.perf_counter() - t0) * 1e6 / reps
+        torch.cuda.synchronize()
+        # the same call marshalled once (PreparedCall): the library and the launch only
+        if headwise:
+            prepared = qk.prepare_headwise(*args, gq, gk, w.eps, 128, 0, *outs)
+        else:
+            prepared = qk.prepare_fused(*args, gq, gk, w.eps, shards, *outs)
+        for _ in range(20):
+            prepared()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            prepared()
+        host_prepared_us = (time.perf_counter() - t0) * 1e6 / reps
+        torch.cuda.synchronize()
         single = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -595,6 +619,12 @@ def latency_table(dev, reps=200):
         b.record()
         b.synchronize()
         b2b_us = a.elapsed_time(b) * 1e3 / reps
+        a.record()
+        for _ in range(reps):
+            prepared()
+        b.record()
+        b.synchronize()
+        b2b_prepared_us = a.elapsed_time(b) * 1e3 / reps
         # The same calls captured in a HIP graph: GPU time per call without
         # the host-side cost of the Python binding.
         side = torch.cuda.Stream()
@@ -628,7 +658,10 @@ def latency_table(dev, reps=200):
                "shards": 1 if headwise else shards, "plan": plan,
                "single_call_us_p10": single[reps // 10], "single_call_us_median": single[reps // 2],
                "single_call_us_p90": single[(9 * reps) // 10],
-               "back_to_back_us": b2b_us, "graph_replay_us": min(graph_us), "bytes": nbytes}
+               "back_to_back_us": b2b_us, "host_us_per_call": host_us, "graph_replay_us": min(graph_us),
+               "bytes": nbytes}
+        row["back_to_back_prepared_us"] = b2b_prepared_us
+        row["host_us_per_call_prepared"] = host_prepared_us
         row["GBps_graph_replay"] = nbytes / (row["graph_replay_us"] * 1e-6) / 1e9
         rows.append(row)
         print(json.dumps(row), flush=True)

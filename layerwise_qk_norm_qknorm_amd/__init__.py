@@ -6,6 +6,7 @@ call does, and raises if the library has not been built.
 """
 
 from .binding import (  # noqa: F401
+    PreparedCall,
     QKNormError,
     abi_version,
     describe_headwise_plan,
@@ -16,4 +17,8 @@ from .binding import (  # noqa: F401
     qknorm_fused,
     qknorm_headwise,
     qknorm_partial_stats,
+    prepare_apply_with_stats,
+    prepare_fused,
+    prepare_headwise,
+    prepare_partial_stats,
 )

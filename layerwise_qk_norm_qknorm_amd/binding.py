@@ -276,6 +276,107 @@ def qknorm_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, 
     return out_q, out_k
 
 
+class PreparedCall:
+    """A library call with its tensors checked and marshalled once.
+
+    Calling it enqueues the same call again, on torch's current stream of the
+    tensors' device (or on ``stream``), with no Python-side checks: for
+    launch loops over fixed buffers (a decode step's Q/K views, say), where
+    the per-call marshalling would cost more host time than the kernel takes
+    on the GPU. The library still validates every launch. The caller keeps
+    the tensors alive and unchanged in shape, stride and place while the
+    object is used (it holds references to them).
+    """
+
+    def __init__(self, fn, args, tensors, device, result):
+        self._fn = fn
+        self._args = args            # ctypes arguments, the stream last
+        self._tensors = tensors      # kept alive with the pointers in _args
+        self._device = device
+        self._result = result
+        torch = _torch_mod()
+        self._raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+    def __call__(self, stream=None):
+        if stream is not None:
+            s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        elif self._raw is not None:
+            s = self._raw(self._device)
+        else:
+            s = _torch_mod().cuda.current_stream(self._device).cuda_stream
+        rc = self._fn(*self._args, s)
+        if rc != QKNORM_OK:
+            _check(rc)
+        return self._result
+
+
+def prepare_fused(q, k, gamma_q, gamma_k, eps, shards=1, out_q=None, out_k=None):
+    """qknorm_fused with its arguments checked and marshalled once (PreparedCall)."""
+    lib = load_library()
+    T = _tokens(q, k)
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, gamma_q, "q")
+    ok = _operand(k, out_k, gamma_k, "k")
+    args = (ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), int(shards))
+    return PreparedCall(lib.qknorm_fused, args, (q, k, gamma_q, gamma_k, out_q, out_k, oq, ok), q.get_device(),
+                        (out_q, out_k))
+
+
+def prepare_apply_with_stats(q, k, gamma_q, gamma_k, eps, stats, hq_full, hk_full, out_q=None, out_k=None):
+    """qknorm_apply_with_stats with its arguments checked and marshalled once (PreparedCall)."""
+    torch = _torch_mod()
+    lib = load_library()
+    T = _tokens(q, k)
+    if stats.dim() != 3 or stats.shape[1] != 2 or stats.shape[2] != T or stats.dtype != torch.float32 \
+            or not stats.is_contiguous():
+        raise ValueError(f"stats must be contiguous float32 [P, 2, {T}]")
+    _rows(q, "q")
+    _same_device(stats, q, "stats")
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, gamma_q, "q")
+    ok = _operand(k, out_k, gamma_k, "k")
+    args = (ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), stats.data_ptr(),
+            int(stats.shape[0]), int(hq_full), int(hk_full))
+    return PreparedCall(lib.qknorm_apply_with_stats, args, (q, k, gamma_q, gamma_k, stats, out_q, out_k, oq, ok),
+                        q.get_device(), (out_q, out_k))
+
+
+def prepare_headwise(q, k, gamma_q, gamma_k, eps, head_dim, gamma_head_stride=0, out_q=None, out_k=None):
+    """qknorm_headwise with its arguments checked and marshalled once (PreparedCall)."""
+    lib = load_library()
+    T = _tokens(q, k)
+    out_q = q if out_q is None else out_q
+    out_k = k if out_k is None else out_k
+    oq = _operand(q, out_q, None, "q")
+    ok = _operand(k, out_k, None, "k")
+    for g, o, name in ((gamma_q, oq, "q"), (gamma_k, ok, "k")):
+        need = (o.h // head_dim - 1) * gamma_head_stride + head_dim if head_dim > 0 else 0
+        if g.dim() != 1 or g.shape[0] < need or (g.shape[0] > 1 and g.stride(0) != 1) or g.dtype != _gamma_dtype(q):
+            raise ValueError(f"gamma for {name} must be contiguous, dtype {_gamma_dtype(q)}, >= {need} elements")
+        _same_device(g, q, "gamma for " + name)
+        o.gamma = g.data_ptr()
+    args = (ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), float(eps), int(head_dim), int(gamma_head_stride))
+    return PreparedCall(lib.qknorm_headwise, args, (q, k, gamma_q, gamma_k, out_q, out_k, oq, ok), q.get_device(),
+                        (out_q, out_k))
+
+
+def prepare_partial_stats(q, k, shards, partials):
+    """qknorm_partial_stats into ``partials`` [S, 2, T], checked and marshalled once (PreparedCall)."""
+    torch = _torch_mod()
+    lib = load_library()
+    T = _tokens(q, k)
+    if (partials.dtype != torch.float32 or tuple(partials.shape) != (shards, 2, T)
+            or not partials.is_contiguous()):
+        raise ValueError(f"partials must be contiguous float32 [{shards}, 2, {T}]")
+    oq = _operand(q, None, None, "q")
+    _same_device(partials, q, "partials")
+    ok = _operand(k, None, None, "k")
+    args = (ctypes.byref(oq), ctypes.byref(ok), T, _dtype_code(q), int(shards), partials.data_ptr())
+    return PreparedCall(lib.qknorm_partial_stats, args, (q, k, partials, oq, ok), q.get_device(), partials)
+
+
 def describe_headwise_plan(hq, hk, T, head_dim, dtype="bf16", gamma_head_stride=0, ld=None):
     """The launch qknorm_headwise would make, for shapes alone (no GPU needed)."""
     lib = load_library()

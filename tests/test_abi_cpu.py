@@ -446,3 +446,28 @@ def test_error_message_is_per_thread():
     q, k = ops()
     q.x = k.x = 0
     assert fused(q, k, T=0) == 0 and last_error() == ""
+
+
+def test_prepared_calls_refuse_host_tensors():
+    """The prepared calls run the binding's checks once, when prepared: a
+    host tensor is refused there, before any library call."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qk.prepare_fused(x[:, :32], x[:, 32:], g, g, 1e-6, 1)
+    with pytest.raises(ValueError):
+        qk.prepare_partial_stats(x[:, :32], x[:, 32:], 1, torch.zeros(1, 2, 4))
+    with pytest.raises(ValueError):
+        qk.prepare_apply_with_stats(x[:, :32], x[:, 32:], g, g, 1e-6, torch.zeros(1, 2, 4), 32, 32)
+
+
+def test_prepared_fused_reaches_the_library_check():
+    """A prepared call whose tensors pass the binding's checks (device
+    stand-ins with NULL data) is refused by the library when called, with
+    nothing launched."""
+    x, g, _ = _fake_case()
+    call = qk.prepare_fused(x[:, :32], x[:, 32:64], g[:32], g[32:64], 1e-6, 1)
+    with pytest.raises(qk.QKNormError) as e:
+        call(stream=0)
+    assert e.value.status == INVALID
