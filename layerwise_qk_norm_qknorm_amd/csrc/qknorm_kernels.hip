@@ -611,6 +611,20 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     const char* xq_row = static_cast<const char*>(a.xq) + tr * a.ldxq * IO::kBytes;
     const char* xk_row = static_cast<const char*>(a.xk) + tr * a.ldxk * IO::kBytes;
 
+    // apply_with_stats: the first planes' statistics are loaded ahead of the
+    // rows, unconditionally (a plane index past the last reloads the last),
+    // so that their latency overlaps the rows' instead of following it.
+    constexpr int kPre = MODE == MODE_APPLY ? 4 : 1;
+    float preq[kPre], prek[kPre];
+    if constexpr (MODE == MODE_APPLY) {
+#pragma unroll
+      for (int p = 0; p < kPre; ++p) {
+        const int pp = p < a.n_planes ? p : a.n_planes - 1;
+        preq[p] = a.stats[(int64_t)(2 * pp) * a.T + tr];
+        prek[p] = a.stats[(int64_t)(2 * pp + 1) * a.T + tr];
+      }
+    }
+
     Chunk xv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
@@ -686,9 +700,14 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       }
     } else {
       // Statistics from outside: planes added in order (the combination step).
-      ssq = a.stats[tr];
-      ssk = a.stats[a.T + tr];
-      for (int p = 1; p < a.n_planes; ++p) {
+      ssq = preq[0];
+      ssk = prek[0];
+#pragma unroll
+      for (int p = 1; p < kPre; ++p) {
+        ssq = p < a.n_planes ? ssq + preq[p] : ssq;
+        ssk = p < a.n_planes ? ssk + prek[p] : ssk;
+      }
+      for (int p = kPre; p < a.n_planes; ++p) {
         ssq += a.stats[(int64_t)(2 * p) * a.T + tr];
         ssk += a.stats[(int64_t)(2 * p + 1) * a.T + tr];
       }
