@@ -62,8 +62,9 @@ def to_device(a, dev):
 # ----------------------------------------------------------------------------- ceiling kernels
 class CeilingLib:
     """ctypes handle of libstreamceil.so: the plain streaming copy and read
-    kernels (16-byte loads, non-temporal 16-byte stores) that give the
-    practical HBM ceiling for the bytes a QK-Norm call moves."""
+    kernels (16-byte loads, ordinary or non-temporal, and non-temporal 16-byte
+    stores) that give the practical HBM ceiling for the bytes a QK-Norm call
+    moves."""
 
     def __init__(self, path=None):
         import ctypes
@@ -73,23 +74,26 @@ class CeilingLib:
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        lib.qkceil_stream.argtypes = [vp, i64, vp, i64, i64, i64, ci, ci, ci, vp, vp]
+        lib.qkceil_stream.argtypes = [vp, i64, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp]
         lib.qkceil_stream.restype = ci
         lib.qkceil_last_error.restype = ctypes.c_char_p
         lib.qkceil_last_error.argtypes = []
         self.lib = lib
 
-    def stream(self, x, ldx, y, ldy, rows, row_bytes, per, block, xk, sink, stream):
-        rc = self.lib.qkceil_stream(x, ldx, y, ldy, rows, row_bytes, per, block, xk, sink, stream)
+    def stream(self, x, ldx, y, ldy, rows, row_bytes, per, block, xk, ntl, sink, stream):
+        rc = self.lib.qkceil_stream(x, ldx, y, ldy, rows, row_bytes, per, block, xk, ntl, sink, stream)
         if rc:
             raise RuntimeError(f"qkceil_stream: {self.lib.qkceil_last_error().decode()}")
 
 
-# (chunks per thread, threads per block, blocks per XCD per run; 0: blocks in
-# order) tried for the ceiling of each call
-CEIL_CONFIGS = ((1, 256, 0), (2, 256, 0), (3, 256, 0), (4, 256, 0), (1, 512, 0), (2, 512, 0), (1, 1024, 0),
+# (chunks per thread, threads per block, blocks per XCD per run (0: blocks in
+# order), non-temporal loads) tried for the ceiling of each call: 12 launch
+# shapes, each with ordinary and with non-temporal loads
+_CEIL_SHAPES = ((1, 256, 0), (2, 256, 0), (3, 256, 0), (4, 256, 0), (1, 512, 0), (2, 512, 0), (1, 1024, 0),
                 (2, 1024, 0), (1, 256, 16), (1, 512, 8), (1, 512, 16), (1, 1024, 16))
-SHAPES_CEIL_CONFIGS = ((1, 256, 0), (1, 512, 0), (2, 512, 0), (1, 512, 16))  # the shapes that win in full sweeps
+CEIL_CONFIGS = tuple(c + (0,) for c in _CEIL_SHAPES) + tuple(c + (1,) for c in _CEIL_SHAPES)
+SHAPES_CEIL_CONFIGS = ((1, 256, 0, 0), (1, 512, 0, 0), (2, 512, 0, 0), (1, 512, 16, 0),
+                       (1, 256, 0, 1), (1, 512, 0, 1), (1, 512, 16, 1), (1, 1024, 16, 1))
 
 
 def _current_stream():
@@ -248,22 +252,24 @@ class ApplyStep(Step):
 class CeilingStep(Step):
     """The streaming ceiling of a call: a plain copy (or read) of exactly the
     Q/K column bytes that `step` moves, over the same rotating buffer sets,
-    with `per` chunks per thread and `block` threads per block."""
+    with `per` chunks per thread and `block` threads per block, runs of `xk`
+    blocks per XCD (0: blocks in order), non-temporal loads if `ntl`."""
 
-    def __init__(self, step, lib, per, block, xk, sink):
+    def __init__(self, step, lib, per, block, xk, ntl, sink):
         self.step, self.lib, self.per, self.block, self.xk, self.sink = step, lib, per, block, xk, sink
+        self.ntl = ntl
         self.n_sets = step.n_sets
         self.copy = step.copy
         self.bytes = step.stream_bytes
         self.launches = len(step.spans(0))
         self.name = f"stream_{'copy' if step.copy else 'read'}(per={per}, block={block}" + \
-            (f", xcd_run={xk})" if xk else ")")
+            (f", xcd_run={xk}" if xk else "") + (", nt loads)" if ntl else ")")
 
     def __call__(self, i):
         st = _current_stream()
         for x, ldx, y, ldy, rows, row_bytes in self.step.spans(i):
             self.lib.stream(x, ldx, y if self.copy else None, ldy, rows, row_bytes, self.per, self.block,
-                            self.xk, self.sink, st)
+                            self.xk, self.ntl, self.sink, st)
 
 
 class ContiguousCopy(Step):
@@ -344,11 +350,12 @@ def ceiling_sweep(step, dev, steps=200, warmup=100, configs=CEIL_CONFIGS, verbos
     lib = CeilingLib()
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     rows = []
-    for per, block, xk in configs:
-        cs = CeilingStep(step, lib, per, block, xk, sink.data_ptr())
+    for per, block, xk, ntl in configs:
+        cs = CeilingStep(step, lib, per, block, xk, ntl, sink.data_ptr())
         _, ev = time_steps(cs, steps, warmup, graph=graph)
         us = ev / steps * 1e6
-        row = {"kernel": cs.name, "per": per, "block": block, "xcd_run": xk, "bytes": cs.bytes, "us": us,
+        row = {"kernel": cs.name, "per": per, "block": block, "xcd_run": xk, "nt_loads": ntl, "bytes": cs.bytes,
+               "us": us,
                "GBps": cs.bytes / (us * 1e-6) / 1e9}
         row["frac_of_peak"] = row["GBps"] / HBM_PEAK_GBPS
         rows.append(row)
@@ -791,7 +798,7 @@ def timeline(dev, reps=5):
         step = step(w, inp, dev, 1) if call == "fused" else step(w, inp, dev)
         plan = _plan_text(binding, w, step.name, 1)
         tpb = int(re.search(r"tokens/block=(\d+)", plan).group(1))
-        cs = CeilingStep(step, ceil, 1, 512, 0, sink.data_ptr())
+        cs = CeilingStep(step, ceil, 1, 512, 0, 1, sink.data_ptr())
         if cs.launches != 1:
             raise RuntimeError(f"{wl}: the ceiling takes {cs.launches} launches; one is timed")
         chunks = step.stream_bytes // (2 if step.copy else 1) // 16
@@ -840,7 +847,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
     ap.add_argument("--ceiling-configs", default="",
-                    help="ceiling launches to sweep, as PERxBLOCK[xXCDRUN],... (default: all of CEIL_CONFIGS)")
+                    help="ceiling launches to sweep, as PERxBLOCK[xXCDRUN[xNTLOADS]],... (default: all of CEIL_CONFIGS)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls from Python instead of one HIP-graph replay of the timed calls")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -927,7 +934,7 @@ def main():
         for n, s in enumerate(steps):
             ceilings[n] = ceiling_sweep(s, dev, steps=max(args.steps, 100), warmup=100, graph=not args.eager,
                                         configs=CEIL_CONFIGS if not args.ceiling_configs else
-                                        [tuple((int(v) for v in (c + "x0").split("x")[:3]))
+                                        [tuple((int(v) for v in (c + "x0x0").split("x")[:4]))
                                          for c in args.ceiling_configs.split(",")])
 
     khash = kernel_source_hash()

@@ -14,15 +14,16 @@
 // loads in flight before its first store. With `xcd_run` = K > 0, each run of
 // 8 K blocks is ordered so that the K blocks the hardware places on one XCD
 // (block i on XCD i mod 8) take K consecutive pieces of the rows (measured up
-// to 1% faster for the GQA prefill bytes with K = 16).
+// to 1% faster for the GQA prefill bytes with K = 16). With `nt_loads` = 1 the
+// loads are non-temporal too, as the QK-Norm kernels' row loads are.
 //
 // C ABI (ctypes from bench.py):
 //   int qkceil_stream(const void* x, int64_t ldx, void* y, int64_t ldy,
 //                     int64_t rows, int64_t row_bytes, int per, int block,
-//                     int xcd_run, void* sink, void* stream);
+//                     int xcd_run, int nt_loads, void* sink, void* stream);
 //     y != NULL: copy; y == NULL: read only (sink: a device word that a
 //     data-dependent test may write, so the loads are not optimised away).
-//     xcd_run: 0 (blocks in order) or 2, 4, 8, 16 (see above).
+//     xcd_run: 0 (blocks in order) or 2, 4, 8, 16 (see above); nt_loads: 0 or 1.
 //     Returns 0, or 1 for an invalid argument (nothing launched) and 3 for a
 //     launch failure; the message is in qkceil_last_error().
 //   const char* qkceil_last_error(void);
@@ -47,7 +48,7 @@ thread_local std::string g_err;
 unsigned long long* g_clocks = nullptr;
 #endif
 
-template <int PER, bool COPY, int XK>
+template <int PER, bool COPY, int XK, bool NTL>
 __global__ void __launch_bounds__(1024) stream_rows(const char* __restrict__ x, int64_t ldx, char* __restrict__ y,
                                                      int64_t ldy, uint32_t nc, uint32_t total,
                                                      uint32_t* __restrict__ sink
@@ -76,7 +77,8 @@ __global__ void __launch_bounds__(1024) stream_rows(const char* __restrict__ x, 
     const uint32_t f = min(first + k * b, total - 1u);
     row[k] = f / nc;
     col[k] = f - row[k] * nc;
-    v[k] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row[k] * ldx + (int64_t)col[k] * 16);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (int64_t)row[k] * ldx + (int64_t)col[k] * 16);
+    v[k] = NTL ? __builtin_nontemporal_load(src) : *src;
   }
   // Every load is issued before the first store: the empty asm takes the
   // loaded registers, so no load can be moved into a store's branch.
@@ -107,29 +109,34 @@ __global__ void __launch_bounds__(1024) stream_rows(const char* __restrict__ x, 
 #endif
 }
 
-template <bool COPY, int XK>
+template <bool COPY, int XK, bool NTL>
 void* pick_per(int per) {
   switch (per) {
-    case 1: return reinterpret_cast<void*>(stream_rows<1, COPY, XK>);
-    case 2: return reinterpret_cast<void*>(stream_rows<2, COPY, XK>);
-    case 3: return reinterpret_cast<void*>(stream_rows<3, COPY, XK>);
-    case 4: return reinterpret_cast<void*>(stream_rows<4, COPY, XK>);
-    case 6: return reinterpret_cast<void*>(stream_rows<6, COPY, XK>);
-    case 8: return reinterpret_cast<void*>(stream_rows<8, COPY, XK>);
+    case 1: return reinterpret_cast<void*>(stream_rows<1, COPY, XK, NTL>);
+    case 2: return reinterpret_cast<void*>(stream_rows<2, COPY, XK, NTL>);
+    case 3: return reinterpret_cast<void*>(stream_rows<3, COPY, XK, NTL>);
+    case 4: return reinterpret_cast<void*>(stream_rows<4, COPY, XK, NTL>);
+    case 6: return reinterpret_cast<void*>(stream_rows<6, COPY, XK, NTL>);
+    case 8: return reinterpret_cast<void*>(stream_rows<8, COPY, XK, NTL>);
+  }
+  return nullptr;
+}
+
+template <bool COPY, bool NTL>
+void* pick_xk(int per, int xk) {
+  switch (xk) {
+    case 0: return pick_per<COPY, 0, NTL>(per);
+    case 2: return pick_per<COPY, 2, NTL>(per);
+    case 4: return pick_per<COPY, 4, NTL>(per);
+    case 8: return pick_per<COPY, 8, NTL>(per);
+    case 16: return pick_per<COPY, 16, NTL>(per);
   }
   return nullptr;
 }
 
 template <bool COPY>
-void* pick(int per, int xk) {
-  switch (xk) {
-    case 0: return pick_per<COPY, 0>(per);
-    case 2: return pick_per<COPY, 2>(per);
-    case 4: return pick_per<COPY, 4>(per);
-    case 8: return pick_per<COPY, 8>(per);
-    case 16: return pick_per<COPY, 16>(per);
-  }
-  return nullptr;
+void* pick(int per, int xk, int ntl) {
+  return ntl ? pick_xk<COPY, true>(per, xk) : pick_xk<COPY, false>(per, xk);
 }
 
 int bad(const char* msg) {
@@ -148,7 +155,7 @@ void qkceil_set_block_clocks(void* clocks) { g_clocks = static_cast<unsigned lon
 #endif
 
 int qkceil_stream(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t row_bytes, int per,
-                  int block, int xcd_run, void* sink, void* stream) {
+                  int block, int xcd_run, int nt_loads, void* sink, void* stream) {
   if (!x || (!y && !sink)) return bad("x, and y or sink, are required");
   if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)sink % 4) return bad("pointers must be 16-byte aligned");
   if (rows < 1 || row_bytes < 16 || row_bytes % 16) return bad("rows >= 1 and row_bytes a positive multiple of 16");
@@ -157,7 +164,8 @@ int qkceil_stream(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows
   if (block < 64 || block > 1024 || block % 64) return bad("block must be a multiple of 64 in [64, 1024]");
   if (xcd_run != 0 && xcd_run != 2 && xcd_run != 4 && xcd_run != 8 && xcd_run != 16)
     return bad("xcd_run must be 0, 2, 4, 8 or 16");
-  void* fn = y ? pick<true>(per, xcd_run) : pick<false>(per, xcd_run);
+  if (nt_loads != 0 && nt_loads != 1) return bad("nt_loads must be 0 or 1");
+  void* fn = y ? pick<true>(per, xcd_run, nt_loads) : pick<false>(per, xcd_run, nt_loads);
   if (!fn) return bad("per must be 1, 2, 3, 4, 6 or 8");
   const int64_t nc = row_bytes / 16;
   const int64_t total = rows * nc;
