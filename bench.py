@@ -798,11 +798,13 @@ def timeline(dev, reps=5):
         step = step(w, inp, dev, 1) if call == "fused" else step(w, inp, dev)
         plan = _plan_text(binding, w, step.name, 1)
         tpb = int(re.search(r"tokens/block=(\d+)", plan).group(1))
+        gl = re.search(r"groups/block=(\d+)", plan)   # blocks that loop over several token groups
+        grid_k = -(-(-(-w.T // tpb)) // (int(gl.group(1)) if gl else 1))
         cs = CeilingStep(step, ceil, 1, 512, 0, 1, sink.data_ptr())
         if cs.launches != 1:
             raise RuntimeError(f"{wl}: the ceiling takes {cs.launches} launches; one is timed")
         chunks = step.stream_bytes // (2 if step.copy else 1) // 16
-        for kind, st, grid, setter in (("kernel", step, -(-w.T // tpb), qk.qknorm_set_block_clocks),
+        for kind, st, grid, setter in (("kernel", step, grid_k, qk.qknorm_set_block_clocks),
                                        ("ceiling", cs, -(-chunks // 512), ceil.lib.qkceil_set_block_clocks)):
             _, ev = time_steps(st, 200, 300, graph=False)   # warm-up, and the eager rate of this build
             runs = []

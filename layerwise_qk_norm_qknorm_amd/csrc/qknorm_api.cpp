@@ -524,6 +524,23 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
     r.lds_bytes = 0;  // static: slots x 64 floats
     r.xrun = 32 / r.tokens_per_block;
   }
+  // FP8 rows, fused and apply_with_stats on the 16-byte path: a launch of one
+  // to four grids of 4096 waves runs as one such grid whose blocks each take
+  // k = ceil(groups / that grid) token groups. The FP8 kernels are bound by
+  // instruction issue, and a block's set-up (slot geometry, gamma loads) is
+  // then paid once per k groups. Alternated on one MI355X against one group
+  // per block: GQA prefill rows (5120/1024, 8192 tokens) 2-3% faster, 3072 to
+  // 6144 tokens 2-7%; the rank-slice apply (1280/256, 12288 to 32768 tokens)
+  // 3-8%; rows of 2048/512 at 8192 tokens 6%, of 8192/1024 at 2048 tokens
+  // 14%; rows of 4096/1024 at 8192 tokens timed 3% slower, inside that
+  // shape's own spread of 10%. Loops over more groups per block were slower
+  // (GQA rows at 16384 tokens 1%, tokens of 3 waves 1-9%), and so were bf16
+  // rows at any such cap (2-7%).
+  if (dtype == kDtypeFP8 && aligned && !r.slot_waves && mode != MODE_STATS) {
+    const int64_t groups = (T + r.tokens_per_block - 1) / r.tokens_per_block;
+    const int64_t c = 4096 / ((r.threads + 63) / 64);
+    if (groups > c && groups <= 4 * c) r.group_loop = (int)((groups + c - 1) / c);
+  }
   *p = r;
   return true;
 }
@@ -688,6 +705,8 @@ std::string describe(const Plan& p) {
                    p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
   if (p.slot_waves && n > 0 && n < (int)sizeof buf)
     snprintf(buf + n, sizeof buf - n, " form=slot-waves threads/block=%d xcd_run=%d", p.threads, p.xrun);
+  if (p.group_loop > 1 && n > 0 && n < (int)sizeof buf)
+    snprintf(buf + n, sizeof buf - n, " groups/block=%d", p.group_loop);
   return buf;
 }
 

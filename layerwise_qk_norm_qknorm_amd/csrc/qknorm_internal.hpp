@@ -77,6 +77,10 @@ struct Plan {
   // tokens
   int slot_waves = 0;
   int xrun = 0;
+  // token groups per block (the grid is ceil(groups / group_loop), so no
+  // block takes more than group_loop of them); 1 except for the FP8 rule in
+  // make_plan
+  int group_loop = 1;
 };
 
 // Kernel arguments (passed by value).

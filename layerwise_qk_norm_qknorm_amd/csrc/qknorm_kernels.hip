@@ -1150,7 +1150,10 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
   // The slot-wave form has no token loop: one block per token group, always
   // (its planner rule admits only launches of at most kMaxGrid blocks).
   const int64_t cap = p.slot_waves ? blocks : grid_cap();
-  const int64_t grid = blocks < cap ? blocks : cap;
+  // Blocks loop over group_loop token groups each where the planner asks for
+  // it (FP8 rows), and over more where the grid is capped.
+  const int64_t want = (blocks + p.group_loop - 1) / p.group_loop;
+  const int64_t grid = want < cap ? want : cap;
   // hipLaunchKernel returns this launch's own status (no sticky error from
   // an earlier, unrelated call is reported as ours).
   RowArgs a = args;

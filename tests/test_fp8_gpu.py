@@ -113,6 +113,56 @@ def test_rank_slice_fp8_partial_and_apply():
     _untouched(host, src, dst, dst_init, hq, hk)
 
 
+@pytest.mark.parametrize("T,k", [(5000, 3), (6144, 3), (4100, 3)])
+def test_gqa_prefill_fp8_token_loop(T, k):
+    """GQA-width FP8 launches whose blocks each take several token groups
+    (groups/block = k; 5000 and 4100 tokens leave some blocks one group
+    short): every element against the oracle, and the split path equal to
+    the fused call bit for bit."""
+    w = I.GQA_PREFILL_FP8.with_T(T)
+    plan = qk.describe_plan(0, w.hq, w.hk, T, "fp8", 1, ld=w.ld)
+    _log(f"[case] {w.key} T={T} plan: {plan}")
+    assert f"groups/block={k}" in plan
+    inp = I.make_inputs(w)
+    out, ref = _fused(inp, w.hv, 1)
+    _compare(out, ref, f"{w.key} T={T}")
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    part = qk.qknorm_partial_stats(xq, xk, 1)
+    aq, ak = torch.empty_like(xq), torch.empty_like(xk)
+    qk.qknorm_apply_with_stats(xq, xk, gq, gk, w.eps, part, w.hq, w.hk, aq, ak)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_np(aq), out[:, :w.hq])
+    assert np.array_equal(torch_to_np(ak), out[:, w.hq:w.hq + w.hk])
+
+
+@pytest.mark.parametrize("T,k", [(12000, 2), (32760, 4)])
+def test_rank_slice_fp8_apply_token_loop(T, k):
+    """The rank-slice apply with blocks taking k groups of 8 tokens (12000
+    tokens: 1500 groups over 750 blocks; 32760: 4095 groups, the last block
+    one group short), 4 planes, every element against the oracle."""
+    w = I.RANK_SLICE_FP8.with_T(T)
+    plan = qk.describe_plan(2, w.hq, w.hk, T, "fp8", 1, ld=w.ld)
+    _log(f"[case] {w.key} apply T={T} plan: {plan}")
+    assert f"groups/block={k}" in plan
+    inp = I.make_inputs(w)
+    hq, hk = w.hq, w.hk
+    host, src, dst = _layout(inp, w.hv)
+    dst_init = dst.host()
+    x, y = src.view(), dst.view()
+    planes = [oracle.qknorm_partial_stats(inp.q, inp.k, "fp8", 1)[0]] + [
+        oracle.qknorm_partial_stats(inp.peer_q[p], inp.peer_k[p], "fp8", 1)[0] for p in range(inp.peer_q.shape[0])]
+    planes = np.stack(planes).astype(np.float32)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    qk.qknorm_apply_with_stats(x[:, :hq], x[:, hq:hq + hk], gq, gk, w.eps, torch.from_numpy(planes).to(DEV),
+                               w.hq_full, w.hk_full, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", w.eps, planes,
+                                         w.hq_full, w.hk_full)
+    _compare(dst.host(), ref, f"rank_slice_fp8 apply T={T}")
+    _untouched(host, src, dst, dst_init, hq, hk)
+
+
 def test_fused_equals_split_fp8_bitwise():
     inp = I.make_custom(300, 2048, 512, 0, "fp8", seed=701)
     xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)

@@ -101,6 +101,17 @@ def test_layerwise_plans_fit_their_kernels(dtype, shards, hq_s, hk_s, T, op, una
     group = min(lanes, 64)
     assert lds == (2 * tpb * (G // group) * 2 * 4 if waves > 1 else 0)
     assert lds <= 64 * 1024
+    # token groups per block: only FP8 rows of the fused and apply calls on
+    # the 16-byte path loop, over 2 to 4 groups, and only when the launch
+    # holds one to four grids of 4096 waves
+    k = int(f.get("groups/block", 1))
+    groups = ceil_div(T, tpb)
+    cap = 4096 // ceil_div(tpb * G, 64)
+    if dtype == "fp8" and aligned and op != 1 and cap < groups <= 4 * cap:
+        assert k == ceil_div(groups, cap)
+    else:
+        assert k == 1, f
+    assert 1 <= k <= 4
 
 
 def feasible_headwise(heads, nc, dtype, aligned):
@@ -179,6 +190,24 @@ def test_mid_size_fused_bf16_plan():
     assert (int(g["lanes/shard"]), int(g["slots"])) == (384, 3), g
     h = fields(qk.describe_plan(0, 4096, 4096, 6144, "bf16", 1, ld=3 * 4096))
     assert (int(h["lanes/shard"]), int(h["slots"])) == (384, 3), h
+
+
+# FP8 launches of one to four grids of 4096 waves loop each block over
+# k = ceil(groups / grid) token groups (2-3% faster for the GQA prefill rows at
+# 8192 tokens, 3-8% for the rank-slice apply on MI355X); larger launches,
+# partial_stats, bf16 rows and the decode sizes keep one group per block.
+def test_fp8_token_loop_plans():
+    def k(op, hq, hk, T, dtype="fp8", ld=None):
+        return int(fields(qk.describe_plan(op, hq, hk, T, dtype, 1, ld=ld or hq + hk + hk)).get("groups/block", 1))
+    assert k(0, 5120, 1024, 8192) == 4        # 2-wave tokens, one per block: 8192 groups over 2048 blocks
+    assert k(0, 5120, 1024, 4096) == 2
+    assert k(0, 5120, 1024, 2048) == 1        # one grid of 4096 waves or less
+    assert k(0, 5120, 1024, 16384) == 1       # more than four grids
+    assert k(2, 1280, 256, 16384) == 2        # rank-slice apply: 8 tokens of 32 lanes per 4-wave block
+    assert k(1, 1280, 256, 16384) == 1        # partial_stats never loops
+    assert k(0, 5120, 1024, 8192, "bf16") == 1
+    assert k(2, 1280, 256, 16384, "bf16") == 1
+    assert k(0, 4096, 4096, 256) == 1         # decode sizes
 
 
 # The split path reproduces the fused call bit for bit only if partial_stats
