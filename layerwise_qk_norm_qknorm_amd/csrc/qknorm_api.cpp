@@ -541,6 +541,20 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
     const int64_t c = 4096 / ((r.threads + 63) / 64);
     if (groups > c && groups <= 4 * c) r.group_loop = (int)((groups + c - 1) / c);
   }
+  // Fused bf16 launches of one shard whose tokens fill 4 waves x 3 chunks
+  // with no idle slot (the GQA prefill rows, 5120/1024), from 6144 tokens:
+  // at most 5 blocks per compute unit instead of the 7 their registers allow.
+  // Fewer reads in flight shorten the wait of each block's last load, and the
+  // memory system keeps up. Alternated on one MI355X against 7 blocks per CU:
+  // 6144 tokens 1.3% faster, 8192 tokens 1.6%, 12288 tokens 1.8%, 16384 tokens
+  // 1.5-1.8% (6 blocks: 0.6-1.0%, 4 blocks: 1.2%). Rows of 4096/1024 (same
+  // token width, a sixth of the slots idle) ran 0.9% slower at 5 blocks and
+  // 0.3% at 6; other widths were unchanged or slower (tokens of 3 waves at 6
+  // blocks +1.8%, of 6 waves at 3 blocks +19%), and so were apply_with_stats
+  // (+0.6% to +4.7%) and partial_stats, so only this shape takes the cap.
+  if (mode == MODE_FUSED && dtype == kDtypeBF16 && aligned && shards == 1 && r.tok_threads == 256 &&
+      r.tokens_per_block == 1 && r.slots == 3 && r.lanes * r.slots == nc && T >= 6144)
+    r.blocks_per_cu = 5;
   *p = r;
   return true;
 }
@@ -685,6 +699,13 @@ bool make_head_plan(int dtype, bool aligned, int64_t head_dim, int64_t heads_q, 
 
 static const char* dtype_name(int d) { return d == kDtypeF32 ? "f32" : d == kDtypeBF16 ? "bf16" : "fp8_e4m3"; }
 
+int launch_lds_bytes(const Plan& p) {
+  constexpr int kLdsPerCu = 160 * 1024;  // gfx950
+  if (p.blocks_per_cu <= 0) return p.lds_bytes;
+  const int pad = kLdsPerCu / p.blocks_per_cu / 2560 * 2560;
+  return pad > p.lds_bytes ? pad : p.lds_bytes;
+}
+
 std::string describe(const Plan& p) {
   if (p.mode == MODE_HEADWISE) {
     char buf[320];
@@ -704,9 +725,11 @@ std::string describe(const Plan& p) {
                    dtype_name(p.dtype), p.aligned ? "16B" : "elementwise", p.shards, p.hq_s, p.hk_s, p.ncq, p.nck,
                    p.lanes, p.tok_threads, p.tokens_per_block, p.waves, p.slots, p.lds_bytes);
   if (p.slot_waves && n > 0 && n < (int)sizeof buf)
-    snprintf(buf + n, sizeof buf - n, " form=slot-waves threads/block=%d xcd_run=%d", p.threads, p.xrun);
+    n += snprintf(buf + n, sizeof buf - n, " form=slot-waves threads/block=%d xcd_run=%d", p.threads, p.xrun);
   if (p.group_loop > 1 && n > 0 && n < (int)sizeof buf)
-    snprintf(buf + n, sizeof buf - n, " groups/block=%d", p.group_loop);
+    n += snprintf(buf + n, sizeof buf - n, " groups/block=%d", p.group_loop);
+  if (p.blocks_per_cu > 0 && n > 0 && n < (int)sizeof buf)
+    snprintf(buf + n, sizeof buf - n, " max_blocks/cu=%d", p.blocks_per_cu);
   return buf;
 }
 

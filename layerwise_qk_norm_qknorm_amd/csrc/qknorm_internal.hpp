@@ -81,6 +81,9 @@ struct Plan {
   // block takes more than group_loop of them); 1 except for the FP8 rule in
   // make_plan
   int group_loop = 1;
+  // at most this many blocks share a compute unit (0: no cap), by padding the
+  // launch's LDS (residency_lds_bytes)
+  int blocks_per_cu = 0;
 };
 
 // Kernel arguments (passed by value).
@@ -153,6 +156,11 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
                Plan* plan, std::string* why);
 
 std::string describe(const Plan& p);
+// The dynamic LDS a launch of `p` asks for: the reduction's own, or, where the
+// plan caps the blocks per compute unit, enough of the 160 KiB LDS that no
+// more than that many blocks fit (a multiple of 2560 bytes, so that the cap
+// holds for any allocation granularity that divides it).
+int launch_lds_bytes(const Plan& p);
 
 // Launches the kernel for `plan` on `stream`. Returns 0 or a HIP error code,
 // with a message in *err.

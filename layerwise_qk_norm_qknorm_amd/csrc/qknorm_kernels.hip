@@ -1163,7 +1163,7 @@ int launch(const Plan& p, const RowArgs& args, void* stream, std::string* err) {
 #endif
   void* kargs[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
-                                       dim3((unsigned)p.threads), kargs, (size_t)p.lds_bytes,
+                                       dim3((unsigned)p.threads), kargs, (size_t)launch_lds_bytes(p),
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     *err = std::string("kernel launch: ") + hipGetErrorString(e);

@@ -112,6 +112,14 @@ def test_layerwise_plans_fit_their_kernels(dtype, shards, hq_s, hk_s, T, op, una
     else:
         assert k == 1, f
     assert 1 <= k <= 4
+    # residency cap: only fused bf16 launches of one shard whose tokens fill
+    # 4 waves x 3 chunks with no idle slot, from 6144 tokens
+    cap = f.get("max_blocks/cu")
+    if op == 0 and dtype == "bf16" and aligned and shards == 1 and G == 256 and tpb == 1 and slots == 3 \
+            and lanes * slots == nc and T >= 6144:
+        assert cap == "5", f
+    else:
+        assert cap is None, f
 
 
 def feasible_headwise(heads, nc, dtype, aligned):
@@ -208,6 +216,23 @@ def test_fp8_token_loop_plans():
     assert k(0, 5120, 1024, 8192, "bf16") == 1
     assert k(2, 1280, 256, 16384, "bf16") == 1
     assert k(0, 4096, 4096, 256) == 1         # decode sizes
+
+
+# GQA-prefill-shaped fused bf16 launches (5120/1024: 4 waves x 3 chunks per
+# token, no idle slot) from 6144 tokens run at most 5 blocks per compute unit
+# (1.3-1.8% faster on MI355X); the same token width with idle slots, fewer
+# tokens, the split calls and FP8 rows keep the register-bound residency.
+def test_gqa_prefill_residency_cap():
+    def cap(op, hq, hk, T, dtype="bf16"):
+        return fields(qk.describe_plan(op, hq, hk, T, dtype, 1, ld=hq + 2 * hk)).get("max_blocks/cu")
+    assert cap(0, 5120, 1024, 8192) == "5"
+    assert cap(0, 5120, 1024, 6144) == "5"
+    assert cap(0, 5120, 1024, 16384) == "5"
+    assert cap(0, 5120, 1024, 4096) is None
+    assert cap(0, 4096, 1024, 8192) is None     # a sixth of the slots idle
+    assert cap(1, 5120, 1024, 8192) is None     # partial_stats
+    assert cap(2, 5120, 1024, 8192) is None     # apply_with_stats
+    assert cap(0, 5120, 1024, 8192, "fp8") is None
 
 
 # The split path reproduces the fused call bit for bit only if partial_stats
