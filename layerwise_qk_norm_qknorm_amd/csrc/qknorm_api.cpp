@@ -535,7 +535,13 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
   // 14%; rows of 4096/1024 at 8192 tokens timed 3% slower, inside that
   // shape's own spread of 10%. Loops over more groups per block were slower
   // (GQA rows at 16384 tokens 1%, tokens of 3 waves 1-9%), and so were bf16
-  // rows at any such cap (2-7%).
+  // rows at any such cap (2-7%). Such launches (up to 4 slots) also hold gamma
+  // widened in registers across a block's tokens (gamma_in_registers): their
+  // grid is resident at 4 waves per SIMD, so the registers cost no
+  // occupancy; GQA prefill rows at 8192 tokens 3.1% faster, the rank-slice
+  // apply 1.4%, rows of 2048/512 1%, GQA rows at 4096 tokens unchanged, where
+  // launches of one group per block lost 1.3-3.4% (the waves per SIMD fall
+  // from 7 to 4).
   if (dtype == kDtypeFP8 && aligned && !r.slot_waves && mode != MODE_STATS) {
     const int64_t groups = (T + r.tokens_per_block - 1) / r.tokens_per_block;
     const int64_t c = 4096 / ((r.threads + 63) / 64);
@@ -727,7 +733,8 @@ std::string describe(const Plan& p) {
   if (p.slot_waves && n > 0 && n < (int)sizeof buf)
     n += snprintf(buf + n, sizeof buf - n, " form=slot-waves threads/block=%d xcd_run=%d", p.threads, p.xrun);
   if (p.group_loop > 1 && n > 0 && n < (int)sizeof buf)
-    n += snprintf(buf + n, sizeof buf - n, " groups/block=%d", p.group_loop);
+    n += snprintf(buf + n, sizeof buf - n, " groups/block=%d%s", p.group_loop,
+                  gamma_in_registers(p) ? " gamma=registers" : "");
   if (p.blocks_per_cu > 0 && n > 0 && n < (int)sizeof buf)
     snprintf(buf + n, sizeof buf - n, " max_blocks/cu=%d", p.blocks_per_cu);
   return buf;

@@ -162,6 +162,14 @@ std::string describe(const Plan& p);
 // holds for any allocation granularity that divides it).
 int launch_lds_bytes(const Plan& p);
 
+// FP8 rows in up to 4 slots, fused or apply_with_stats on the 16-byte path,
+// blocks looping over several token groups: the row kernel holds gamma
+// widened to float32 in registers across the block's tokens.
+inline bool gamma_in_registers(const Plan& p) {
+  return p.dtype == kDtypeFP8 && p.aligned && !p.slot_waves && p.group_loop > 1 && p.slots <= 4 &&
+         (p.mode == MODE_FUSED || p.mode == MODE_APPLY);
+}
+
 // Launches the kernel for `plan` on `stream`. Returns 0 or a HIP error code,
 // with a message in *err.
 int launch(const Plan& plan, const RowArgs& args, void* stream, std::string* err);

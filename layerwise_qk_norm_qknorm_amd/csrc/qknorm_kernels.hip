@@ -309,61 +309,75 @@ constexpr bool head_sums_by_dot() {
   return IO::kBytes < 4 && V > (IO::kBytes == 2 ? 2 : 4);
 }
 
+// Phase B and the final scaling of FP8 rows in up to 4 slots: y = (x * gamma)
+// * r[i], one rounding to E4M3, stores of the valid chunks (slot i goes to the
+// Q or the K row). The saturating conversion costs four operations per
+// element, so each chunk is converted without it and stored at once, four
+// results at a time (no chunk's float32 results outlive its conversion),
+// while the lane tracks its largest magnitude; only if some lane of the wave
+// saw a result beyond 448 or a NaN does the wave convert its chunks again,
+// saturated, and store them over the first results (a lane's two stores to
+// one address land in program order). `gamma_at(i, e)` is element e of slot
+// i's gamma as float32: widened from the packed bf16 words where it is used,
+// or read from registers that hold it widened across tokens.
+template <class IO, int V, bool ALIGNED, class GammaAt>
+__device__ __forceinline__ void scale_store_fp8(const Chunk (&xv)[V], GammaAt gamma_at, const float (&r)[V],
+                                                const bool (&isq)[V], const int (&col)[V], const int (&cnt)[V],
+                                                char* yq_row, char* yk_row, bool active) {
+  constexpr int VW = IO::kVW;
+  float big = 0.0f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    Chunk out;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {  // elements 4p .. 4p+3: one word of x
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], true);
+      const float y0 = (lo[0] * gamma_at(i, 4 * p)) * r[i];
+      const float y1 = (lo[1] * gamma_at(i, 4 * p + 1)) * r[i];
+      const float y2 = (hi[0] * gamma_at(i, 4 * p + 2)) * r[i];
+      const float y3 = (hi[1] * gamma_at(i, 4 * p + 3)) * r[i];
+      float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(big, __builtin_fabsf(y0)),
+                                              __builtin_fabsf(y1));
+      m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(y2)), __builtin_fabsf(y3));
+      big = cnt[i] > 0 ? m : big;  // idle slots left out
+      out.w[p] = pack_fp8_word(y0, y1, y2, y3);
+      // The word is formed here, not sunk into the store's branch (which
+      // would keep all of the chunk's float32 results live until then).
+      asm volatile("" : "+v"(out.w[p]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+  }
+  // A NaN (from gamma, say) sends the wave through the saturating path too,
+  // which keeps NaN and clamps the rest.
+  if (__builtin_amdgcn_ballot_w64(active && !(big <= 448.0f)) != 0) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float xf[VW], y[VW];
+      decode<IO>(xv[i], xf);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) y[e] = sat_e4m3((xf[e] * gamma_at(i, e)) * r[i]);
+      Chunk out;
+      pack<IO>(out, y);
+      if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
+    }
+  }
+}
+
 // Phase B and the final scaling for this lane's chunks of one token:
 // y = (x * gamma) * r[i], one rounding to the I/O type, stores of the valid
-// chunks (slot i goes to the Q or the K row). For FP8 the saturating
-// conversion costs four operations per element, so with up to 4 slots each
-// chunk is converted without it and stored at once, four results at a time
-// (no chunk's float32 results outlive its conversion), while the lane tracks
-// its largest magnitude; only if some lane of the wave saw a result beyond
-// 448 or a NaN does the wave convert its chunks again, saturated, and store
-// them over the first results (a lane's two stores to one address land in
-// program order).
+// chunks (slot i goes to the Q or the K row); FP8 rows in up to 4 slots take
+// scale_store_fp8.
 template <class IO, int V, bool ALIGNED>
 __device__ __forceinline__ void scale_store(const Chunk (&xv)[V], const GChunk<IO> (&g)[V], const float (&r)[V],
                                             const bool (&isq)[V], const int (&col)[V], const int (&cnt)[V],
                                             char* yq_row, char* yk_row, bool active) {
   constexpr int VW = IO::kVW;
-  if (IO::kDtype == kDtypeFP8 && V <= 4) {
-    float big = 0.0f;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      Chunk out;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {  // elements 4p .. 4p+3: one word of x, two of gamma
-        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], false);
-        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(xv[i].w[p], true);
-        const float y0 = (lo[0] * bf16_lo(g[i].w[2 * p])) * r[i];
-        const float y1 = (lo[1] * bf16_hi(g[i].w[2 * p])) * r[i];
-        const float y2 = (hi[0] * bf16_lo(g[i].w[2 * p + 1])) * r[i];
-        const float y3 = (hi[1] * bf16_hi(g[i].w[2 * p + 1])) * r[i];
-        float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(big, __builtin_fabsf(y0)),
-                                                __builtin_fabsf(y1));
-        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(y2)), __builtin_fabsf(y3));
-        big = cnt[i] > 0 ? m : big;  // idle slots left out
-        out.w[p] = pack_fp8_word(y0, y1, y2, y3);
-        // The word is formed here, not sunk into the store's branch (which
-        // would keep all of the chunk's float32 results live until then).
-        asm volatile("" : "+v"(out.w[p]));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
-    }
-    // A NaN (from gamma, say) sends the wave through the saturating path too,
-    // which keeps NaN and clamps the rest.
-    if (__builtin_amdgcn_ballot_w64(active && !(big <= 448.0f)) != 0) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        float xf[VW], gf[VW], y[VW];
-        decode<IO>(xv[i], xf);
-        decode_gamma<IO>(g[i], gf);
-#pragma unroll
-        for (int e = 0; e < VW; ++e) y[e] = sat_e4m3((xf[e] * gf[e]) * r[i]);
-        Chunk out;
-        pack<IO>(out, y);
-        if (active && cnt[i] > 0) store_chunk<IO, ALIGNED>(isq[i] ? yq_row : yk_row, col[i], cnt[i], out);
-      }
-    }
+  if constexpr (IO::kDtype == kDtypeFP8 && V <= 4) {
+    // element e of a chunk's gamma: the low or high bf16 half of word e / 2
+    const auto gamma_at = [&](int i, int e) { return (e & 1) ? bf16_hi(g[i].w[e >> 1]) : bf16_lo(g[i].w[e >> 1]); };
+    scale_store_fp8<IO, V, ALIGNED>(xv, gamma_at, r, isq, col, cnt, yq_row, yk_row, active);
   } else {
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -531,8 +545,16 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 // to a block only at one wave each), so the token index and all row
 // arithmetic are wave-uniform and run on the scalar unit; the general form
 // (WW false) also holds several shards and tokens that share a wave.
-template <class IO, int V, int MODE, bool ALIGNED, bool WW>
+// GW (FP8 rows in up to 4 slots, fused and apply modes, 16-byte path): gamma
+// is widened to float32 once per block and held in registers across the
+// block's tokens, instead of kept packed and widened for every token. That
+// takes about 50 more VGPRs (4 waves per SIMD instead of 7), so only launches
+// whose blocks loop over several token groups take it (the planner's FP8
+// token loop, whose whole grid is resident at 4 waves per SIMD).
+template <class IO, int V, int MODE, bool ALIGNED, bool WW, bool GW = false>
 __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED)) qknorm_rows(const RowArgs a) {
+  static_assert(!GW || (IO::kDtype == kDtypeFP8 && MODE != MODE_STATS && ALIGNED && V <= 4),
+                "widened gamma: FP8 rows, fused or apply, 16-byte path, up to 4 slots");
   extern __shared__ float red[];  // [2 buffers][tokens per block][groups per token] float2 (Q, K)
 #ifdef QKNORM_BLOCK_CLOCKS
   clock_begin(a.clocks);
@@ -574,6 +596,11 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
 #pragma unroll
     for (int i = 0; i < V; ++i)
       g[i] = load_gamma<IO, ALIGNED>(static_cast<const char*>(isq[i] ? a.gq : a.gk), col[i], max(cnt[i], 1));
+  }
+  float gw[GW ? V : 1][GW ? IO::kVW : 1];  // GW: gamma widened once per block
+  if constexpr (GW) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) decode_gamma<IO>(g[i], gw[i]);
   }
 
   const int group = a.group;            // butterfly width: min(L, 64)
@@ -642,7 +669,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     Chunk xv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) xv[i] = load_chunk<IO, ALIGNED>(isq[i] ? xq_row : xk_row, col[i], max(cnt[i], 1));
-    if (MODE != MODE_STATS && IO::kBytes < 4) {
+    if (MODE != MODE_STATS && IO::kBytes < 4 && !GW) {
 #pragma unroll
       for (int i = 0; i < V; ++i) keep_packed(g[i]);
     }
@@ -742,7 +769,12 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
       for (int i = 0; i < V; ++i) rr[i] = isq[i] ? rq : rk;
       char* yq_row = static_cast<char*>(a.yq) + tr * a.ldyq * IO::kBytes;
       char* yk_row = static_cast<char*>(a.yk) + tr * a.ldyk * IO::kBytes;
-      scale_store<IO, V, ALIGNED>(xv, g, rr, isq, col, cnt, yq_row, yk_row, active);
+      if constexpr (GW) {
+        const auto gamma_at = [&](int i, int e) { return gw[i][e]; };
+        scale_store_fp8<IO, V, ALIGNED>(xv, gamma_at, rr, isq, col, cnt, yq_row, yk_row, active);
+      } else {
+        scale_store<IO, V, ALIGNED>(xv, g, rr, isq, col, cnt, yq_row, yk_row, active);
+      }
     }
   }
 #ifdef QKNORM_BLOCK_CLOCKS
@@ -1041,6 +1073,18 @@ KernelFn pick_slots(int v) {
 
 // The scalar-token form serves partial_stats and fused FP8 rows on the
 // 16-byte path only; the element-wise path is the general kernel.
+// FP8 rows with gamma held widened in registers (GW): 1 to 4 slots.
+template <int MODE, bool WW>
+KernelFn pick_gw_slots(int v) {
+  switch (v) {
+    case 1: return qknorm_rows<FP8, 1, MODE, true, WW, true>;
+    case 2: return qknorm_rows<FP8, 2, MODE, true, WW, true>;
+    case 3: return qknorm_rows<FP8, 3, MODE, true, WW, true>;
+    case 4: return qknorm_rows<FP8, 4, MODE, true, WW, true>;
+  }
+  return nullptr;
+}
+
 template <class IO, int MODE>
 KernelFn pick_aligned(bool aligned, bool ww, int v) {
   if (!aligned) return pick_slots<IO, MODE, false, false>(v);
@@ -1124,6 +1168,10 @@ KernelFn pick_kernel(const Plan& p) {
   // they are memory-bound and the scalar row arithmetic adds latency).
   const bool ww = (p.mode == MODE_STATS || (p.mode == MODE_FUSED && p.dtype == kDtypeFP8)) && p.shards == 1 &&
                   p.tok_threads % 64 == 0 && (p.tokens_per_block == 1 || p.tok_threads == 64);
+  if (gamma_in_registers(p)) {
+    if (p.mode == MODE_APPLY) return pick_gw_slots<MODE_APPLY, false>(p.slots);
+    return ww ? pick_gw_slots<MODE_FUSED, true>(p.slots) : pick_gw_slots<MODE_FUSED, false>(p.slots);
+  }
   switch (p.dtype) {
     case kDtypeBF16: return pick_mode<BF16>(p.mode, p.aligned, ww, p.slots);
     case kDtypeF32: return pick_mode<F32>(p.mode, p.aligned, ww, p.slots);

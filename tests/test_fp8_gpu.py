@@ -241,6 +241,39 @@ def test_fp8_nan_gamma_with_overflow():
     _compare(out, ref, "fp8 NaN gamma")
 
 
+@pytest.mark.parametrize("op", [0, 2])
+def test_fp8_gamma_in_registers_saturation_and_nan(op):
+    """Looping FP8 launches hold gamma widened in registers (plan: gamma=
+    registers): a gamma of 300 with one NaN column there too, fused (op 0) and
+    apply_with_stats (op 2) at 4500 tokens of the GQA widths (3 groups per
+    block): NaN stays in its column, results beyond 448 saturate."""
+    T, hq, hk = 4500, 5120, 1024
+    plan = qk.describe_plan(op, hq, hk, T, "fp8", 1, ld=hq)
+    _log(f"[case] fp8 gamma in registers op={op} T={T} plan: {plan}")
+    assert "groups/block=3" in plan and "gamma=registers" in plan
+    inp = I.make_custom(T, hq, hk, 0, "fp8", seed=803 + op)
+    g = np.full(hq, 300.0)
+    g[5] = np.nan
+    inp.gamma_q[...] = I.to_bf16_bits(g)
+    xq, xk = np_to_torch(inp.q).to(DEV), np_to_torch(inp.k).to(DEV)
+    gq, gk = np_to_torch(inp.gamma_q).to(DEV), np_to_torch(inp.gamma_k).to(DEV)
+    yq, yk = torch.empty_like(xq), torch.empty_like(xk)
+    if op == 0:
+        qk.qknorm_fused(xq, xk, gq, gk, 1e-6, 1, yq, yk)
+        ref = oracle.qknorm_fused(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", 1e-6, 1)
+    else:
+        planes = oracle.qknorm_partial_stats(inp.q, inp.k, "fp8", 1).astype(np.float32)
+        qk.qknorm_apply_with_stats(xq, xk, gq, gk, 1e-6, torch.from_numpy(planes).to(DEV), hq, hk, yq, yk)
+        ref = oracle.qknorm_apply_with_stats(inp.q, inp.k, inp.gamma_q, inp.gamma_k, "fp8", 1e-6, planes, hq, hk)
+    torch.cuda.synchronize()
+    out = np.concatenate([torch_to_np(yq), torch_to_np(yk)], axis=1)
+    assert np.all((out[:, 5] & 0x7F) == 0x7F)
+    big = np.abs(ref.yq) > 464
+    assert big.sum() > 100000
+    assert np.all((out[:, :hq][big] & 0x7F) == 0x7E)
+    _compare(out, ref, f"fp8 gamma in registers op={op}")
+
+
 def test_fp8_elementwise_path():
     _compare(*_fused(I.make_custom(45, 40 * 8, 24, 0, "fp8", seed=901), 8, 1, offset=3), "fp8 misaligned")
     _compare(*_fused(I.make_custom(31, 1000, 200, 0, "fp8", seed=902), 0, 4, ld_pad=1), "fp8 odd stride")

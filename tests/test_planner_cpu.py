@@ -216,6 +216,11 @@ def test_fp8_token_loop_plans():
     assert k(0, 5120, 1024, 8192, "bf16") == 1
     assert k(2, 1280, 256, 16384, "bf16") == 1
     assert k(0, 4096, 4096, 256) == 1         # decode sizes
+    # looping launches of up to 4 slots hold gamma widened in registers
+    def gr(op, hq, hk, T):
+        return "gamma=registers" in qk.describe_plan(op, hq, hk, T, "fp8", 1, ld=hq + 2 * hk)
+    assert gr(0, 5120, 1024, 8192) and gr(2, 1280, 256, 16384)
+    assert not gr(0, 5120, 1024, 16384) and not gr(0, 5120, 1024, 2048) and not gr(1, 1280, 256, 16384)
 
 
 # GQA-prefill-shaped fused bf16 launches (5120/1024: 4 waves x 3 chunks per
