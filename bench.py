@@ -688,7 +688,8 @@ def shapes_table(dev, T=8192, steps=100):
     call from Python costs more host time than the kernel takes, so
     back-to-back launches, `us_back_to_back`, do not keep the GPU busy).
     `ceiling_us` is the streaming ceiling of the same bytes (the copy kernel
-    of libstreamceil.so over the same buffers, best of three launch shapes)."""
+    of libstreamceil.so over the same buffers, best of the launch shapes in
+    SHAPES_CEIL_CONFIGS)."""
     import torch
     import layerwise_qk_norm_qknorm_amd as qk
     from layerwise_qk_norm_qknorm_amd import inputs as I
