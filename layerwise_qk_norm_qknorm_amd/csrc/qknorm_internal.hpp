@@ -82,7 +82,7 @@ struct Plan {
   // make_plan
   int group_loop = 1;
   // at most this many blocks share a compute unit (0: no cap), by padding the
-  // launch's LDS (residency_lds_bytes)
+  // launch's LDS (launch_lds_bytes)
   int blocks_per_cu = 0;
 };
 
