@@ -1232,7 +1232,8 @@ int launch_heads(const Plan& p, const HeadArgs& args, void* stream, std::string*
   }
   const int64_t blocks = (args.T + p.tokens_per_block - 1) / p.tokens_per_block;
   const int64_t cap = grid_cap();
-  const int64_t grid = blocks < cap ? blocks : cap;
+  const int64_t want = (blocks + p.group_loop - 1) / p.group_loop;  // FP8 rows: two groups per block
+  const int64_t grid = want < cap ? want : cap;
   HeadArgs a = args;
   void* kargs[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),

@@ -274,6 +274,28 @@ def test_fp8_gamma_in_registers_saturation_and_nan(op):
     _compare(out, ref, f"fp8 gamma in registers op={op}")
 
 
+@pytest.mark.parametrize("T", [4501, 8192])
+def test_fp8_headwise_two_groups_per_block(T):
+    """FP8 headwise launches from 4096 tokens: blocks take two token groups
+    (4501 tokens: the last block one), 128-wide heads of the GQA widths,
+    every element against the oracle."""
+    w = I.GQA_PREFILL_FP8.with_T(T)
+    plan = qk.describe_headwise_plan(w.hq, w.hk, T, 128, "fp8", 0, ld=w.ld)
+    _log(f"[case] fp8 headwise T={T} plan: {plan}")
+    assert "groups/block=2" in plan
+    inp = I.make_inputs(w)
+    hq, hk = w.hq, w.hk
+    host, src, dst = _layout(inp, w.hv)
+    dst_init = dst.host()
+    x, y = src.view(), dst.view()
+    gq, gk = np_to_torch(inp.gamma_q[:128]).to(DEV), np_to_torch(inp.gamma_k[:128]).to(DEV)
+    qk.qknorm_headwise(x[:, :hq], x[:, hq:hq + hk], gq, gk, w.eps, 128, 0, y[:, :hq], y[:, hq:hq + hk])
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_headwise(inp.q, inp.k, inp.gamma_q[:128], inp.gamma_k[:128], "fp8", w.eps, 128, 0)
+    _compare(dst.host(), ref, f"fp8 headwise T={T}")
+    _untouched(host, src, dst, dst_init, hq, hk)
+
+
 def test_fp8_elementwise_path():
     _compare(*_fused(I.make_custom(45, 40 * 8, 24, 0, "fp8", seed=901), 8, 1, offset=3), "fp8 misaligned")
     _compare(*_fused(I.make_custom(31, 1000, 200, 0, "fp8", seed=902), 0, 4, ld_pad=1), "fp8 odd stride")
