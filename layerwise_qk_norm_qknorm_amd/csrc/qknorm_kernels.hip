@@ -610,17 +610,18 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
   const int64_t step = (int64_t)gridDim.x * tpb;
   int buf = 0;
 
-  // Token groups follow blockIdx, except for partial_stats and the fused
-  // call: there each run of 64 blocks is transposed as 8 x 8, so that the 8
-  // blocks the hardware places on one XCD (block i goes to XCD i mod 8) take
-  // 8 consecutive token groups. For partial_stats their sums share cache
-  // lines of the partials, and a line is written from one L2 (2-3% faster);
-  // the fused call measured 1.4% faster on the GQA prefill (bf16, 8192
-  // tokens), 0.5% on its FP8 rows and 1.6% on 256-token decode rows, with
-  // runs of 2 to 16 blocks per XCD all within 0.3% of each other (rank-slice
-  // rows 0.3% slower); apply_with_stats gained nothing and keeps blockIdx
-  // order. Each block still covers every gridDim-th group after its first,
-  // so every group is covered once.
+  // Token groups follow blockIdx, except that each run of 64 blocks is
+  // transposed as 8 x 8, so that the 8 blocks the hardware places on one XCD
+  // (block i goes to XCD i mod 8) take 8 consecutive token groups. For
+  // partial_stats their sums share cache lines of the partials, and a line
+  // is written from one L2 (2-3% faster); the fused call measured 1.4%
+  // faster on the GQA prefill (bf16, 8192 tokens), 0.5% on its FP8 rows and
+  // 1.6% on 256-token decode rows, with runs of 2 to 16 blocks per XCD all
+  // within 0.3% of each other (rank-slice rows 0.3% slower); apply_with_stats
+  // reads each statistics line from one L2 instead of several, and with
+  // non-temporal row loads ran 1.3% faster on the rank slice (bf16), 2.9%
+  // (FP8) and 0.3% at 32768 tokens. Each block still covers every
+  // gridDim-th group after its first, so every group is covered once.
   // Large fused and apply launches: the blocks of the first resident
   // generation issue their gamma loads and then start their rows at 8
   // staggered times, 128 clocks apart (groups of 8 consecutive blocks, one
@@ -639,7 +640,7 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
     }
   }
   int64_t g0 = blockIdx.x;
-  if ((MODE == MODE_STATS || MODE == MODE_FUSED) && (int64_t)blockIdx.x < ((int64_t)gridDim.x & ~(int64_t)63)) {
+  if ((int64_t)blockIdx.x < ((int64_t)gridDim.x & ~(int64_t)63)) {
     const int r64 = blockIdx.x & 63;
     g0 = ((int64_t)blockIdx.x & ~(int64_t)63) | ((r64 & 7) << 3) | (r64 >> 3);
   }
