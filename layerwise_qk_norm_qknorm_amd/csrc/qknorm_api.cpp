@@ -512,7 +512,7 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
   // 2 to 4 chunks per lane on the 16-byte path (the rank slices) takes the
   // slot-wave form: the same lanes, slots and sums, with each chunk loaded by
   // a thread of its own in row order and the sums exchanged in LDS; a block
-  // holds one wave's worth of tokens, and each XCD takes runs of 64
+  // holds one wave's worth of tokens, and each XCD takes runs of 128
   // consecutive tokens (whole 128-byte lines of the partial planes). It has
   // no token loop, so it takes launches of at most 2^30 tokens (one block per
   // token group).
@@ -522,7 +522,7 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
     r.tokens_per_block = 64 / r.lanes;
     r.threads = 64 * r.slots;
     r.lds_bytes = 0;  // static: slots x 64 floats
-    r.xrun = 64 / r.tokens_per_block;
+    r.xrun = 128 / r.tokens_per_block;
   }
   // FP8 rows, fused and apply_with_stats on the 16-byte path: a launch of one
   // to four grids of 4096 waves runs as one such grid whose blocks each take

@@ -966,9 +966,10 @@ __global__ void __launch_bounds__(max_threads_for_slots(V, IO::kDtype, ALIGNED))
 // (the split path's bit-for-bit agreement with the fused call rests on it).
 // Runs of 8 * XRUN blocks are ordered so that the blocks the hardware places
 // on one XCD (block i on XCD i mod 8) take XRUN consecutive token groups,
-// 64 tokens, whose sums fill two whole 128-byte lines of each partial plane
-// in one L2 (runs of 64 tokens measured 1.7% faster than runs of 32 on the
-// FP8 rank slice and equal on bf16; runs of 16 were 0.6-1.6% slower). A wave here lives for one load, and everything before the load
+// 128 tokens, whose sums fill four whole 128-byte lines of each partial
+// plane in one L2 (alternated on one MI355X on the rank slice: runs of 64
+// tokens 1.7% faster than runs of 32 on FP8 rows and equal on bf16, runs of
+// 128 another 0.3% (FP8) and 0.8% (bf16); runs of 16 were 0.6-1.6% slower). A wave here lives for one load, and everything before the load
 // delays it: only the address is formed first (on the scalar unit as far as
 // the block's rows go), the reducing wave's work waits until after the
 // exchange, and there is no token loop (one block per token group). Measured
@@ -982,7 +983,7 @@ template <class IO, int V, int L>
 __global__ void __launch_bounds__(64 * V) qknorm_stats_slot_waves(const RowArgs a) {
   constexpr int NCL = L * V;          // chunk positions per token (the ones past the row idle)
   constexpr int TPW = 64 / L;         // tokens per block
-  constexpr int XRUN = 64 / TPW;      // blocks per XCD per run: 64 tokens
+  constexpr int XRUN = 128 / TPW;     // blocks per XCD per run: 128 tokens
   constexpr int64_t RUN = 8 * XRUN;   // a power of two
   __shared__ float cs[TPW * NCL];     // chunk sums, token by token in row order
 #ifdef QKNORM_BLOCK_CLOCKS

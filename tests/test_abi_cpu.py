@@ -198,14 +198,14 @@ def test_describe_plans_of_the_workloads():
     d = qk.describe_plan(OP_FUSED, 1280, 256, 16384, "bf16", 1, ld=1792)
     assert "path=16B" in d and "slots=3" in d and "waves/token=1" in d and "tokens/block=4" in d
     # its partial_stats: the same lanes and slots in the slot-wave form (one
-    # wave per slot, a chunk per thread, a token per block, runs of 64 tokens
-    # per XCD); FP8 rows: two 32-lane tokens per block, runs of 32 blocks
+    # wave per slot, a chunk per thread, a token per block, runs of 128 tokens
+    # per XCD); FP8 rows: two 32-lane tokens per block, runs of 64 blocks
     d = qk.describe_plan(OP_PARTIAL_STATS, 1280, 256, 16384, "bf16", 1, ld=1792)
     assert "lanes/shard=64" in d and "slots=3" in d and "form=slot-waves" in d and "tokens/block=1" in d
-    assert "threads/block=192" in d and "xcd_run=64" in d
+    assert "threads/block=192" in d and "xcd_run=128" in d
     d = qk.describe_plan(OP_PARTIAL_STATS, 1280, 256, 16384, "fp8", 1, ld=1792)
     assert "lanes/shard=32" in d and "slots=3" in d and "form=slot-waves" in d and "tokens/block=2" in d
-    assert "xcd_run=32" in d
+    assert "xcd_run=64" in d
     # a single decode token is spread over 8 waves, two chunks per lane
     d = qk.describe_plan(OP_FUSED, 4096, 4096, 1, "bf16", 1, ld=12288)
     assert "slots=2" in d and "waves/token=8" in d

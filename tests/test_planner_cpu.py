@@ -94,7 +94,7 @@ def test_layerwise_plans_fit_their_kernels(dtype, shards, hq_s, hk_s, T, op, una
         # chunk slot of a wave's lanes, one wave's worth of tokens per block
         assert op == 1 and shards == 1 and aligned and lanes in (32, 64) and 2 <= slots <= 4
         assert tpb == 64 // lanes and int(f["threads/block"]) == 64 * slots and lds == 0
-        assert int(f["xcd_run"]) * tpb == 64
+        assert int(f["xcd_run"]) * tpb == 128
         return
     assert tpb * G <= max_threads(slots, dtype, aligned)
     waves = ceil_div(G, 64)

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # T, hq, hk, dtype, packed rows (separate Q and K arrays take the general kernel)
-    (16384 + 37, 1280, 256, "bf16", True),   # the rank slice's widths; 37 tokens past the last run of 512
+    (16384 + 37, 1280, 256, "bf16", True),   # the rank slice's widths; 37 tokens past the last run of 1024
     (1025, 1280, 256, "fp8", True),          # two tokens per block, the last block's second token absent
     (4097, 512, 256, "f32", True),           # fp32 rows, 64 lanes x 3
     (3000, 768, 256, "bf16", True),          # 32 lanes x 4
