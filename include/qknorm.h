@@ -229,8 +229,9 @@ int qknorm_abi_version(void);
 /*
  * qknorm_describe_plan -- writes a one-line description of the launch the
  * given call would make (element-wise or 16-byte path, lanes per shard,
- * chunks per lane, waves per token) into buf (NUL-terminated, truncated to
- * len). Validates like the call itself (op selects which one; `shards` is
+ * chunks per lane, waves per token, and where they apply: token groups per
+ * block, gamma held widened in registers, a cap on blocks per compute unit)
+ * into buf (NUL-terminated, truncated to len). Validates like the call itself (op selects which one; `shards` is
  * ignored for QKNORM_OP_APPLY_WITH_STATS) and makes no HIP call, so it works
  * without a GPU. Device pointers are only compared, never dereferenced.
  */
