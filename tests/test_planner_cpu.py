@@ -380,3 +380,27 @@ def test_per_head_prefill_plans_are_the_measured_best():
         f = fields(qk.describe_headwise_plan(hq, hk, 8192, hd, dtype, 0, ld=hq + 2 * hk))
         assert f["layout"] == "per-head"
         assert (int(f["lanes/head"]), int(f["slots"])) == (lanes, slots), (dtype, hd, hq, hk, f)
+
+
+# The large-token cases of the random GPU sweep reach every launch rule that
+# only applies from thousands of tokens (checked here on the CPU, from the
+# plans those cases describe).
+def test_large_random_cases_cover_the_launch_rules():
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "random_shapes", os.path.join(os.path.dirname(__file__), "test_random_shapes_gpu.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    seen = set()
+    for c in m.large_cases():
+        ld = c["hq"] + c["hk"] + c["hv"]
+        if c["op"] == "headwise":
+            d = qk.describe_headwise_plan(c["hq"], c["hk"], c["T"], 128, c["dtype"], 0, ld=ld)
+            seen |= {"headwise loop"} if "groups/block=2" in d else set()
+        else:
+            d = qk.describe_plan(0 if c["op"] == "fused" else 2, c["hq"], c["hk"], c["T"], c["dtype"], 1, ld=ld)
+            seen |= {f for f in ("groups/block", "gamma=registers", "max_blocks/cu") if f in d}
+            if c["op"] == "split" and "gamma=registers" in d:
+                seen.add("split gamma=registers")
+    assert seen >= {"headwise loop", "groups/block", "gamma=registers", "max_blocks/cu", "split gamma=registers"}, seen

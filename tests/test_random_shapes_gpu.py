@@ -62,9 +62,54 @@ def _case(i):
                 offset=offset, in_place=in_place, seed=7000 + i)
 
 
+# Launches of several thousand tokens, where the planner's loop, residency and
+# register rules take effect (FP8 blocks over 2-4 token groups with gamma in
+# registers, FP8 headwise blocks over 2 groups, GQA-shaped bf16 launches at
+# 5 blocks per CU): 16 seeded cases of the GQA-like and rank-slice widths and
+# random ones, at token counts that leave the last block's loop short.
+N_LARGE = 16
+LARGE_WIDTHS = ((5120, 1024), (4096, 1024), (2048, 512), (1280, 256), (3072, 1024))
+
+
+def _large_case(i):
+    rng = np.random.default_rng(9000 + i)
+    dtype = ["bf16", "fp8", "fp8", "f32"][rng.integers(0, 4)]
+    op = ["fused", "split", "headwise"][rng.integers(0, 3)]
+    vw = VW[dtype]
+    hq, hk = LARGE_WIDTHS[int(rng.integers(0, len(LARGE_WIDTHS)))]
+    if rng.random() < 0.25:
+        hq, hk = int(rng.integers(8, 400)) * vw, int(rng.integers(2, 100)) * vw
+        hq, hk = hq - hq % 128 or 128, hk - hk % 128 or 128
+    T = int(rng.choice([4097, 5000, 6144, 6500, 8191]))
+    if i == 0:  # the GQA prefill shape at a ragged token count: the residency cap
+        dtype, op, hq, hk, T = "bf16", "fused", 5120, 1024, 6500
+    return dict(dtype=dtype, op=op, shards=1, hq=hq, hk=hk, head_dim=128 if op == "headwise" else 0, T=T,
+                hv=int(rng.choice([0, 128])), ld_pad=0, offset=int(rng.choice([0, 0, 3])),
+                in_place=bool(rng.random() < 0.25), seed=9000 + i)
+
+
+def large_cases():
+    return [_large_case(i) for i in range(N_LARGE)]
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_token_case(i):
+    c = _large_case(i)
+    if c["op"] == "headwise":
+        plan = qk.describe_headwise_plan(c["hq"], c["hk"], c["T"], 128, c["dtype"], 0, ld=c["hq"] + c["hk"] + c["hv"])
+    else:
+        plan = qk.describe_plan(0 if c["op"] == "fused" else 2, c["hq"], c["hk"], c["T"], c["dtype"], 1,
+                                ld=c["hq"] + c["hk"] + c["hv"])
+    print(f"[case] large {i}: {c} plan: {plan}", flush=True)
+    _run(c, f"large {i}")
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i):
-    c = _case(i)
+    _run(_case(i), str(i))
+
+
+def _run(c, i):
     dtype, op, S, hq, hk, T = c["dtype"], c["op"], c["shards"], c["hq"], c["hk"], c["T"]
     inp = I.make_custom(T, hq, hk, 0, dtype, seed=c["seed"])
     ld = hq + hk + c["hv"] + c["ld_pad"]
