@@ -547,19 +547,23 @@ bool make_plan(int mode, int dtype, bool aligned, bool packed, int shards, int64
     const int64_t c = 4096 / ((r.threads + 63) / 64);
     if (groups > c && groups <= 4 * c) r.group_loop = (int)((groups + c - 1) / c);
   }
-  // Fused bf16 launches of one shard whose tokens fill 4 waves x 3 chunks
-  // with no idle slot (the GQA prefill rows, 5120/1024), from 6144 tokens:
-  // at most 5 blocks per compute unit instead of the 7 their registers allow.
-  // Fewer reads in flight shorten the wait of each block's last load, and the
-  // memory system keeps up. Alternated on one MI355X against 7 blocks per CU:
-  // 6144 tokens 1.3% faster, 8192 tokens 1.6%, 12288 tokens 1.8%, 16384 tokens
-  // 1.5-1.8% (6 blocks: 0.6-1.0%, 4 blocks: 1.2%). Rows of 4096/1024 (same
-  // token width, a sixth of the slots idle) ran 0.9% slower at 5 blocks and
-  // 0.3% at 6; other widths were unchanged or slower (tokens of 3 waves at 6
-  // blocks +1.8%, of 6 waves at 3 blocks +19%), and so were apply_with_stats
-  // (+0.6% to +4.7%) and partial_stats, so only this shape takes the cap.
-  if (mode == MODE_FUSED && dtype == kDtypeBF16 && aligned && shards == 1 && r.tok_threads == 256 &&
-      r.tokens_per_block == 1 && r.slots == 3 && r.lanes * r.slots == nc && T >= 6144)
+  // Fused bf16 launches of one shard whose tokens fill 4 waves x 3 chunks or
+  // 3 waves x 4 chunks with no idle slot (the GQA prefill rows, 5120/1024:
+  // the prefill layout and, up to 4096 tokens, the mid-size one), from 3072
+  // tokens: at most 5 blocks per compute unit instead of the 7 (or 10) their
+  // registers allow. Fewer reads in flight shorten the wait of each block's
+  // last load, and the memory system keeps up. Alternated on one MI355X
+  // against the register-bound residency: 3072 tokens 1.3% faster, 4096
+  // 0.9%, 5000 1.4%, 6144 1.3%, 8192 1.6%, 12288 1.8%, 16384 1.5-1.8% (6
+  // blocks: 0.4-1.6%, 4 blocks at 8192 tokens: 1.2%). Rows of 4096/1024 (4
+  // waves, a sixth of the slots idle) ran 0.9% slower at 5 blocks and 0.3% at
+  // 6; other widths were unchanged or slower (tokens of 3 waves x 3 chunks at
+  // 6 blocks +1.8%, of 6 waves at 3 blocks +19%), and so were
+  // apply_with_stats (+0.6% to +4.7%) and partial_stats, so only this shape
+  // takes the cap.
+  if (mode == MODE_FUSED && dtype == kDtypeBF16 && aligned && shards == 1 && r.tokens_per_block == 1 &&
+      ((r.tok_threads == 256 && r.slots == 3) || (r.tok_threads == 192 && r.slots == 4)) &&
+      r.lanes * r.slots == nc && T >= 3072)
     r.blocks_per_cu = 5;
   *p = r;
   return true;
